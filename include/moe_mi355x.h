@@ -1,0 +1,183 @@
+/*
+ * moe_mi355x.h -- C ABI of the fused two-stage MXFP4 mixture-of-experts FFN for MI355X
+ * (gfx950), library libmoe_mi355x.so.
+ *
+ * The operator (github ROCm/aiter PR 6259 "Motivation"/"Technical Details", PR 5118
+ * "Summary", PR 4463 "What", PR 4471 "Technical Details"):
+ *   1. moe_sort      groups routed rows (token t, slot k) by expert and pads each expert to a
+ *                    whole tile of block_m rows (PR 5118, "Summary": moe_sorting);
+ *   2. moe_quant_act encodes bf16 activations as fp8 e4m3 or fp4 e2m1 codes with one e8m0
+ *                    scale per 32 elements (PR 6259 "Test Result": fp8_blockwise_1x32;
+ *                    PR 4463 "What": the fp4x2 activation dtype);
+ *   3. moe_fused     Stage1: gathered rows x [gate|up] MXFP4 weights with the SiTUv2 epilogue
+ *                    y = beta*tanh(g/beta)*sigmoid(g) * lb*tanh(u/lb) (PR 6259 "Motivation"),
+ *                    tanh evaluated as 2*sigmoid(2x)-1 (PR 4471 "Technical Details");
+ *                    the intermediate re-encoded in the activation dtype; Stage2: MXFP4
+ *                    down-projection, times the router weight, summed into each token's row.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates or frees device memory and keeps no pointer after a call returns; it holds no
+ *     mutable global state, so calls from several host threads are safe.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work on
+ *     it and never synchronizes; results are ready when the stream reaches that point.
+ *   - Arguments are validated on the host before anything is enqueued.  On a validation error
+ *     nothing is launched and the output buffers are untouched.  MOE_ERR_HIP means a launch
+ *     failed; hipGetLastError() was cleared and its value is returned by moe_last_hip_error().
+ *   - Layouts are row-major and densely packed.  fp4x2 packs two e2m1 codes per byte, the
+ *     element with the even index in the low nibble.  e8m0 scale byte s means 2^(s-127).
+ *   - fp8 is OCP E4M3FN (bias 7, max 448, no infinities).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad enum value */
+  MOE_ERR_UNSUPPORTED = 2,   /* a shape or option the kernels do not implement */
+  MOE_ERR_CAPACITY = 3,      /* layout capacity smaller than moe_cap_tiles() */
+  MOE_ERR_HIP = 4,           /* a HIP launch failed */
+  MOE_ERR_WORKSPACE = 5      /* workspace smaller than the *_ws_bytes() helper requires */
+} moe_status_t;
+
+typedef enum { MOE_DT_BF16 = 0, MOE_DT_FP8_E4M3 = 1, MOE_DT_FP4_E2M1 = 2 } moe_dtype_t;
+
+/* Activation of the stage1 epilogue.  SITUV2 and SILU take act(g) * up as described above
+ * (SILU: y = silu(g) * u, PR 4471 "Motivation").  NONE_TEST is a test hook: moe_fused runs
+ * Stage1 only and writes the raw fp32 gate and up sums of every routed row to the workspace
+ * (see moe_fused_debug_offset); `out` is not written.  Any other value -> MOE_ERR_UNSUPPORTED
+ * (PR 4471 "Technical Details": reject activations other than silu and situv2). */
+typedef enum { MOE_ACT_SITUV2 = 0, MOE_ACT_SILU = 1, MOE_ACT_NONE_TEST = 2 } moe_act_t;
+
+/* There are no default betas: PR 4463 "Three tuner defects" item 1 shows two sides silently
+ * using different defaults.  beta and linear_beta must be finite and > 0 for SITUV2. */
+typedef struct {
+  int32_t act;          /* moe_act_t */
+  float beta;           /* SiTUv2 beta (4.0 on the pages) */
+  float linear_beta;    /* SiTUv2 linear_beta (25.0 on the pages) */
+} moe_act_params_t;
+
+/* Padded expert-major layout written by moe_sort and read by moe_fused.
+ * Routed row (t, k) is named by its flat index v = t*topk + k.  For each local expert e in
+ * ascending order, its rows are listed in ascending v and padded with the sentinel T*topk to a
+ * multiple of block_m; experts without rows get no tile.  Tile i holds rows
+ * [i*block_m, (i+1)*block_m) of sorted_token_ids and belongs to expert expert_ids[i]. */
+typedef struct {
+  int32_t *sorted_token_ids; /* [cap_tiles*block_m] v, or T*topk on padding and unused tiles */
+  float *sorted_weights;     /* [cap_tiles*block_m] topk_w[v], 0 on padding; may be NULL */
+  int32_t *expert_ids;       /* [cap_tiles] local expert of each tile, -1 past num_tiles */
+  int32_t *num_tiles;        /* [1] number of used tiles; written on the device only */
+  int32_t cap_tiles;         /* tiles the buffers hold, >= moe_cap_tiles(...) */
+  int32_t block_m;           /* rows per tile: 16 or 32 */
+} moe_layout_t;
+
+/* Tiles needed in the worst case: sum_e ceil(c_e/bm) <= ceil(T*topk/bm) + min(E, T*topk). */
+static inline int32_t moe_cap_tiles(int32_t tokens, int32_t topk, int32_t num_local_experts,
+                                    int32_t block_m) {
+  int64_t n = (int64_t)tokens * topk;
+  int64_t e = num_local_experts < n ? num_local_experts : n;
+  return (int32_t)((n + block_m - 1) / block_m + e);
+}
+
+/* Routed rows are counted in chunks of this many flat indices. */
+#define MOE_SORT_CHUNK 4096
+
+static inline size_t moe_align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+/* Workspace of moe_sort: per-chunk expert counts and per-row ranks (int32). */
+static inline size_t moe_sort_ws_bytes(int32_t tokens, int32_t topk, int32_t num_local_experts) {
+  int64_t n = (int64_t)tokens * topk;
+  int64_t chunks = (n + MOE_SORT_CHUNK - 1) / MOE_SORT_CHUNK;
+  return moe_align256((size_t)chunks * (size_t)num_local_experts * 4) + moe_align256((size_t)n * 4);
+}
+
+/* Bytes of one intermediate row of inter_dim elements in dtype dt (codes only). */
+static inline size_t moe_row_bytes(int32_t cols, int32_t dt) {
+  return dt == MOE_DT_BF16 ? (size_t)cols * 2 : dt == MOE_DT_FP8_E4M3 ? (size_t)cols : (size_t)cols / 2;
+}
+
+/* Workspace of moe_fused: an fp32 [T, D] combine accumulator, the stage1 intermediate
+ * [cap*bm, I] in a_dtype plus its [cap*bm, I/32] e8m0 scales (fp8/fp4), and for NONE_TEST a
+ * fp32 [cap*bm, 2I] debug area holding the raw gate (cols 0..I-1) and up (I..2I-1) sums. */
+static inline size_t moe_fused_debug_offset(int32_t tokens, int32_t model_dim, int32_t inter_dim,
+                                            int32_t cap_tiles, int32_t block_m, int32_t a_dtype) {
+  size_t rows = (size_t)cap_tiles * block_m;
+  return moe_align256((size_t)tokens * model_dim * 4) +
+         moe_align256(rows * moe_row_bytes(inter_dim, a_dtype)) +
+         moe_align256(a_dtype == MOE_DT_BF16 ? 0 : rows * (size_t)(inter_dim / 32));
+}
+
+static inline size_t moe_fused_ws_bytes(int32_t tokens, int32_t model_dim, int32_t inter_dim,
+                                        int32_t cap_tiles, int32_t block_m, int32_t a_dtype,
+                                        int32_t act) {
+  size_t b = moe_fused_debug_offset(tokens, model_dim, inter_dim, cap_tiles, block_m, a_dtype);
+  if (act == MOE_ACT_NONE_TEST) b += moe_align256((size_t)cap_tiles * block_m * inter_dim * 2 * 4);
+  return b;
+}
+
+/* moe_sort -- build the padded expert-major layout (PR 5118 "Summary"; PR 6259 Stage1 input).
+ *   topk_ids  [tokens, topk] int32 global expert ids; ids outside
+ *             [expert_begin, expert_begin + num_local_experts) (including -1) are skipped.
+ *   topk_w    [tokens, topk] fp32 router weights, or NULL; required iff
+ *             layout->sorted_weights is non-NULL.
+ *   layout    buffers to fill; cap_tiles >= moe_cap_tiles(tokens, topk, num_local_experts,
+ *             block_m), block_m in {16, 32}.  Every entry of all four buffers is written.
+ *   ws        device scratch of ws_bytes >= moe_sort_ws_bytes(tokens, topk, num_local_experts).
+ * The result is unique and bit-exact: it does not depend on launch order or timing.
+ * Limits: 1 <= tokens*topk < 2^31, 1 <= num_local_experts <= 8192. */
+moe_status_t moe_sort(const int32_t *topk_ids, const float *topk_w, int32_t tokens, int32_t topk,
+                      int32_t expert_begin, int32_t num_local_experts, const moe_layout_t *layout,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* moe_quant_act -- 1x32 block quantization of bf16 rows (PR 6259 "Test Result"; PR 4463).
+ *   x_bf16    [rows, cols] bf16 bit patterns, cols % 32 == 0.
+ *   dt        MOE_DT_FP8_E4M3 -> q_out [rows, cols] bytes; MOE_DT_FP4_E2M1 -> q_out
+ *             [rows, cols/2] fp4x2 bytes.  MOE_DT_BF16 -> MOE_ERR_INVALID_ARG.
+ *   scale_out [rows, cols/32] e8m0 bytes.
+ * Rule per block of 32 (OCP MX shared scale): amax = max|x|; amax == 0 -> scale byte 0 and
+ * every element +-0; else sexp = clamp(floor(log2 amax) - emax, -127, 127) (emax 8 for e4m3, 2
+ * for e2m1), scale byte sexp + 127, each element x / 2^sexp rounded to nearest, ties to even,
+ * saturating at +-448 / +-6; the sign bit is kept.  A block holding Inf or NaN gets scale byte
+ * 255 (NaN) and element codes 0. */
+moe_status_t moe_quant_act(const uint16_t *x_bf16, int64_t rows, int64_t cols, int32_t dt,
+                           void *q_out, uint8_t *scale_out, void *stream);
+
+/* moe_fused -- Stage1 + Stage2 over a layout from moe_sort.
+ *   x         activations [tokens, D]: bf16 (a_dtype BF16), fp8 bytes (FP8) or fp4x2 bytes
+ *             [tokens, D/2] (FP4), as moe_quant_act writes them.
+ *   x_scale   [tokens, D/32] e8m0 for FP8 / FP4; must be NULL for BF16.
+ *   w1, w1_scale  [E, 2I, D/2] fp4x2 and [E, 2I, D/32] e8m0: rows 0..I-1 gate, I..2I-1 up.
+ *   w2, w2_scale  [E, D, I/2] fp4x2 and [E, D, I/32] e8m0.
+ *   topk_w    [tokens, topk] fp32 router weights; row v of the layout is scaled by topk_w[v].
+ *   layout    from moe_sort with the same tokens/topk/E; cap_tiles and block_m as there.
+ *   act       activation and betas (no defaults).
+ *   out_bf16  [tokens, D] bf16, overwritten; tokens with no local expert get zeros.
+ *   ws        scratch of ws_bytes >= moe_fused_ws_bytes(...).
+ * Shapes: D % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED: every K step is one
+ * 128-deep block-scaled MFMA); E >= 1.  Stage1 uses fp32 accumulation; the intermediate is
+ * stored as bf16 (BF16) or re-encoded with the moe_quant_act rule (FP8, FP4); Stage2
+ * accumulates in fp32 and the per-token sum uses fp32 atomics, so the last bits of `out` may
+ * differ from run to run. */
+moe_status_t moe_fused(const void *x, const uint8_t *x_scale, int32_t a_dtype,
+                       const uint8_t *w1, const uint8_t *w1_scale,
+                       const uint8_t *w2, const uint8_t *w2_scale,
+                       const float *topk_w, const moe_layout_t *layout,
+                       int32_t tokens, int32_t topk, int32_t num_local_experts,
+                       int32_t model_dim, int32_t inter_dim, const moe_act_params_t *act,
+                       uint16_t *out_bf16, void *ws, size_t ws_bytes, void *stream);
+
+/* The hipError_t value behind the last MOE_ERR_HIP returned on this thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

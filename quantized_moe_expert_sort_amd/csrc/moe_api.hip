@@ -1,0 +1,128 @@
+// extern "C" entry points of libmoe_mi355x.so: argument validation on the host, then the
+// kernel launchers.  Nothing here allocates, synchronizes or keeps state between calls except
+// the thread-local copy of the last HIP error.
+#include <cmath>
+
+#include "moe_kernels.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+moe_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = (int32_t)e;
+  return MOE_ERR_HIP;
+}
+
+bool valid_dtype(int32_t dt) { return dt == MOE_DT_BF16 || dt == MOE_DT_FP8_E4M3 || dt == MOE_DT_FP4_E2M1; }
+
+moe_status_t check_layout(const moe_layout_t* L, int32_t tokens, int32_t topk, int32_t E) {
+  if (!L || !L->sorted_token_ids || !L->expert_ids || !L->num_tiles) return MOE_ERR_INVALID_ARG;
+  if (L->block_m != 16 && L->block_m != 32) return MOE_ERR_UNSUPPORTED;
+  if (L->cap_tiles < 0 || L->cap_tiles < moe_cap_tiles(tokens, topk, E, L->block_m)) return MOE_ERR_CAPACITY;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+moe_status_t moe_sort(const int32_t* topk_ids, const float* topk_w, int32_t tokens, int32_t topk,
+                      int32_t expert_begin, int32_t num_local_experts, const moe_layout_t* layout,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (tokens < 0 || topk < 1 || num_local_experts < 1) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)tokens * topk >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (num_local_experts > moe::MAX_SORT_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (tokens > 0 && !topk_ids) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = check_layout(layout, tokens, topk, num_local_experts);
+  if (st != MOE_OK) return st;
+  if (layout->sorted_weights && tokens > 0 && !topk_w) return MOE_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)tokens * topk;
+  if (n > MOE_SORT_CHUNK) {
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe_sort_ws_bytes(tokens, topk, num_local_experts)) return MOE_ERR_WORKSPACE;
+  }
+  moe::SortLayout L{layout->sorted_token_ids, layout->sorted_weights, layout->expert_ids,
+                    layout->num_tiles, layout->cap_tiles};
+  return hip_status(moe::launch_sort(topk_ids, topk_w, n, expert_begin, num_local_experts,
+                                     layout->block_m, L, ws, (hipStream_t)stream));
+}
+
+moe_status_t moe_quant_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, int32_t dt, void* q_out,
+                           uint8_t* scale_out, void* stream) {
+  if (dt != MOE_DT_FP8_E4M3 && dt != MOE_DT_FP4_E2M1) return MOE_ERR_INVALID_ARG;
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x_bf16 || !q_out || !scale_out) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_quant_act(x_bf16, rows, cols, dt, q_out, scale_out, (hipStream_t)stream));
+}
+
+moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
+                       const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                       const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
+                       int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
+                       const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!valid_dtype(a_dtype)) return MOE_ERR_INVALID_ARG;
+  if (!act) return MOE_ERR_INVALID_ARG;
+  if (act->act != MOE_ACT_SITUV2 && act->act != MOE_ACT_SILU && act->act != MOE_ACT_NONE_TEST)
+    return MOE_ERR_UNSUPPORTED;
+  if (act->act == MOE_ACT_SITUV2 &&
+      !(std::isfinite(act->beta) && act->beta > 0.f && std::isfinite(act->linear_beta) && act->linear_beta > 0.f))
+    return MOE_ERR_INVALID_ARG;
+  if (tokens < 0 || topk < 1 || num_local_experts < 1 || model_dim <= 0 || inter_dim <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (model_dim % 128 != 0 || inter_dim % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)tokens * topk >= ((int64_t)1 << 31) || (int64_t)tokens * model_dim >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
+  moe_status_t st = check_layout(layout, tokens, topk, num_local_experts);
+  if (st != MOE_OK) return st;
+  if ((int64_t)layout->cap_tiles * layout->block_m >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (tokens == 0) return MOE_OK;
+  if (!x || !w1 || !w1_scale || !w2 || !w2_scale || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if ((a_dtype == MOE_DT_BF16) != (x_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (act->act != MOE_ACT_NONE_TEST && !out_bf16) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe_fused_ws_bytes(tokens, model_dim, inter_dim, layout->cap_tiles, layout->block_m,
+                                    a_dtype, act->act))
+    return MOE_ERR_WORKSPACE;
+
+  const size_t rows = (size_t)layout->cap_tiles * layout->block_m;
+  uint8_t* base = (uint8_t*)ws;
+  const size_t off_inter = moe_align256((size_t)tokens * model_dim * 4);
+  const size_t off_iscale = off_inter + moe_align256(rows * moe_row_bytes(inter_dim, a_dtype));
+  const size_t off_dbg = moe_fused_debug_offset(tokens, model_dim, inter_dim, layout->cap_tiles,
+                                                layout->block_m, a_dtype);
+  moe::FusedArgs a;
+  a.x = (const uint8_t*)x;
+  a.xs = x_scale;
+  a.w1 = w1;
+  a.w1s = w1_scale;
+  a.w2 = w2;
+  a.w2s = w2_scale;
+  a.topk_w = topk_w;
+  a.sorted_ids = layout->sorted_token_ids;
+  a.expert_ids = layout->expert_ids;
+  a.num_tiles = layout->num_tiles;
+  a.acc = (float*)base;
+  a.inter = base + off_inter;
+  a.inter_s = a_dtype == MOE_DT_BF16 ? nullptr : base + off_iscale;
+  a.dbg = act->act == MOE_ACT_NONE_TEST ? (float*)(base + off_dbg) : nullptr;
+  a.out = out_bf16;
+  a.T = tokens;
+  a.topk = topk;
+  a.E = num_local_experts;
+  a.D = model_dim;
+  a.I = inter_dim;
+  a.cap_tiles = layout->cap_tiles;
+  a.block_m = layout->block_m;
+  a.a_dtype = a_dtype;
+  a.act = act->act;
+  a.beta = act->beta;
+  a.linear_beta = act->linear_beta;
+  return hip_status(moe::launch_fused(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

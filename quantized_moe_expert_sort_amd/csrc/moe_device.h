@@ -1,0 +1,160 @@
+// Device-side building blocks for the gfx950 MoE kernels: matrix-core operand types, the
+// block-scaled MFMA wrappers, the fp4 -> bf16 dequantizer, SiTUv2 / SiLU, and the 1x32
+// e8m0 block encoder.  Everything here is written for CDNA4 wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+enum : int { DT_BF16 = 0, DT_FP8 = 1, DT_FP4 = 2 };
+enum : int { ACT_SITUV2 = 0, ACT_SILU = 1, ACT_NONE = 2 };
+
+// Operand format codes of v_mfma_scale_f32_16x16x128_f8f6f4 (cbsz / blgp fields).
+enum : int { MFMA_FMT_FP8 = 0, MFMA_FMT_FP4 = 4 };
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------------ matrix-core operand layout
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4, lane l = 16*g + r (r = l % 16, g = l / 16):
+//   fp4 operand: dwords 0..3 hold K elements [32g, 32g+32) of row r, element 2i in the low
+//                nibble of byte i; dwords 4..7 are ignored.
+//   fp8 operand: dwords 0..3 hold K [16g, 16g+16), dwords 4..7 hold K [64+16g, 64+16g+16).
+//   scale byte (selected by opsel) of lane l scales row r, K block [32g, 32g+32).
+// v_mfma_f32_16x16x32_bf16: lane l holds K [8g, 8g+8) of row r.
+// Both: accumulator element i of lane l is C[4g + i][r].
+
+__device__ __forceinline__ v4f mfma_fp8_fp4(const v8i& a, const v8i& b, const v4f& c,
+                                            uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, MFMA_FMT_FP8, MFMA_FMT_FP4, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ v4f mfma_fp4_fp4(const v8i& a, const v8i& b, const v4f& c,
+                                            uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, MFMA_FMT_FP4, MFMA_FMT_FP4, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// e8m0 byte -> the float 2^(s-127) (only its exponent is read by the scaled converts).
+__device__ __forceinline__ float e8m0_to_float(uint32_t s) {
+  return s == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(s << 23);
+}
+
+// Eight e2m1 codes (one dword, element 2i in the low nibble of byte i) -> eight bf16 values
+// times 2^(s-127), exact for every finite scale that keeps the result a bf16 normal.
+__device__ __forceinline__ v8bf fp4x8_to_bf16(uint32_t q, float scale) {
+  v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0);
+  v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1);
+  v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2);
+  v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3);
+  v8bf r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ v8bf as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  u4 t = {a, b, c, d};
+  return __builtin_bit_cast(v8bf, t);
+}
+
+// ------------------------------------------------------------------ activations
+//
+// sigmoid over the exp2 / reciprocal fast path; tanh(x) = 2*sigmoid(2x) - 1, which saturates to
+// +-1 without clamping (github ROCm/aiter PR 4471, "Technical Details").
+
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+__device__ __forceinline__ float fast_tanh(float x) { return 2.0f * fast_sigmoid(2.0f * x) - 1.0f; }
+
+// SiTUv2 (github ROCm/aiter PR 6259, "Motivation"):
+//   y = beta*tanh(g/beta)*sigmoid(g) * lb*tanh(u/lb); inv_* are 1/beta and 1/lb.
+__device__ __forceinline__ float situv2(float g, float u, float beta, float inv_beta, float lb,
+                                        float inv_lb) {
+  return beta * fast_tanh(g * inv_beta) * fast_sigmoid(g) * (lb * fast_tanh(u * inv_lb));
+}
+
+// SiLU epilogue (github ROCm/aiter PR 4471, "Motivation"): silu(g) * u.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * fast_sigmoid(g) * u; }
+
+// ------------------------------------------------------------------ 1x32 block encoder
+//
+// OCP MX shared-scale rule, evaluated in integers so that every input (normal or subnormal)
+// is encoded exactly: the block exponent is floor(log2 amax) - emax clamped to [-127, 127],
+// elements are rounded to nearest (ties to the even code) and saturate at the largest finite.
+
+struct Fp8Fmt { static constexpr int MBITS = 3, EMIN = -6, EMAX = 8, MAXCODE = 126, SIGN = 0x80; };
+struct Fp4Fmt { static constexpr int MBITS = 1, EMIN = 0, EMAX = 2, MAXCODE = 7, SIGN = 0x8; };
+
+// Block exponent from the bit pattern of amax (finite, > 0).
+template <class F>
+__device__ __forceinline__ int block_sexp(uint32_t amax_bits) {
+  int e = amax_bits >= 0x00800000u ? (int)(amax_bits >> 23) - 127 : (31 - __clz(amax_bits)) - 149;
+  e -= F::EMAX;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Magnitude code of |v| (bit pattern abits, finite) divided by 2^sexp.
+template <class F>
+__device__ __forceinline__ uint32_t encode_mag(uint32_t abits, int sexp) {
+  if (abits == 0) return 0;
+  uint32_t m;
+  int e;                                   // |v| = m * 2^e, m < 2^24
+  if (abits >= 0x00800000u) { m = (abits & 0x7FFFFFu) | 0x800000u; e = (int)(abits >> 23) - 150; }
+  else { m = abits; e = -149; }
+  const int L = (31 - __clz(m)) + e - sexp;            // floor(log2(|v| / 2^sexp))
+  const int Lc = L > F::EMIN ? L : F::EMIN;            // subnormals share the lowest binade
+  const int shift = (Lc - F::MBITS) - (e - sexp);      // quanta of size 2^(Lc - MBITS)
+  uint32_t n;
+  if (shift <= 0) {
+    n = m << (-shift);
+  } else if (shift > 31) {
+    n = 0;
+  } else {
+    n = m >> shift;
+    const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    n += (rem > half || (rem == half && (n & 1u))) ? 1u : 0u;
+  }
+  const uint32_t code = ((uint32_t)(Lc - F::EMIN + 1) << F::MBITS) + n - (1u << F::MBITS);
+  return code < (uint32_t)F::MAXCODE ? code : (uint32_t)F::MAXCODE;
+}
+
+// Reduce |v| bit patterns over the 32 lanes of a half-wave (xor shuffles stay inside it).
+__device__ __forceinline__ uint32_t halfwave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, m, WAVE);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Encode one element per lane of a 32-lane block (lanes 32h .. 32h+31 form a block).
+// Returns the element code; *scale_byte receives the block's e8m0 byte.
+template <class F>
+__device__ __forceinline__ uint32_t block_encode_lane(float v, uint32_t* scale_byte) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t abits = bits & 0x7FFFFFFFu;
+  const uint32_t amax = halfwave_max_u32(abits);
+  const uint32_t sign = (bits >> 31) ? (uint32_t)F::SIGN : 0u;
+  if (amax >= 0x7F800000u) { *scale_byte = 255u; return 0u; }          // Inf / NaN in block
+  if (amax == 0u) { *scale_byte = 0u; return sign; }
+  const int sexp = block_sexp<F>(amax);
+  *scale_byte = (uint32_t)(sexp + 127);
+  return encode_mag<F>(abits, sexp) | sign;
+}
+
+}  // namespace moe

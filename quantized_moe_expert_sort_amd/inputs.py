@@ -16,7 +16,9 @@ Workload shapes follow the tuned wide-MoE shape of the source pages (896 experts
 model_dim 3584, inter_dim 384 per tensor-parallel shard, or 112 local experts with inter_dim
 3072 per expert-parallel rank).
 """
+import concurrent.futures
 import math
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -149,19 +151,25 @@ def make_mxfp4_expert(seed, tensor_id, e, N, K):
     return packed.astype(np.uint8), _SCALE_BYTES[sidx]
 
 
-def make_mxfp4(seed, tensor_id, E, N, K):
-    packed = np.empty((E, N, K // 2), dtype=np.uint8)
-    scales = np.empty((E, N, K // 32), dtype=np.uint8)
-    for e in range(E):
-        packed[e], scales[e] = make_mxfp4_expert(seed, tensor_id, e, N, K)
+def make_mxfp4(seed, tensor_id, E, N, K, experts=None):
+    """Experts 0..E-1 (or the listed ones, in that order) of one MXFP4 weight tensor."""
+    ids = list(range(E)) if experts is None else list(experts)
+    packed = np.empty((len(ids), N, K // 2), dtype=np.uint8)
+    scales = np.empty((len(ids), N, K // 32), dtype=np.uint8)
+
+    def one(i):
+        packed[i], scales[i] = make_mxfp4_expert(seed, tensor_id, ids[i], N, K)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(one, range(len(ids))))
     return packed, scales
 
 
-def make_weights(seed, E, D, I):
+def make_weights(seed, E, D, I, experts=None):
     """w1 [E, 2I, D/2] + [E, 2I, D/32] (gate rows 0..I-1, up rows I..2I-1) and
-    w2 [E, D, I/2] + [E, D, I/32]."""
-    w1, w1s = make_mxfp4(seed, _W1, E, 2 * I, D)
-    w2, w2s = make_mxfp4(seed, _W2, E, D, I)
+    w2 [E, D, I/2] + [E, D, I/32]; with `experts`, only those experts, in that order."""
+    w1, w1s = make_mxfp4(seed, _W1, E, 2 * I, D, experts)
+    w2, w2s = make_mxfp4(seed, _W2, E, D, I, experts)
     return w1, w1s, w2, w2s
 
 

@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports every entry point its header declares, and rejects bad
+arguments on the host with the documented status codes before launching anything.
+
+Validation cases pass placeholder device pointers, so they run only where no GPU is visible
+(a case whose check failed to fire would otherwise launch kernels on those pointers)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import quantized_moe_expert_sort_amd as qm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_mi355x.h")
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="placeholder pointers: CPU-only checks")
+
+P = ctypes.c_void_p(0x100000)          # placeholder device pointer (never dereferenced)
+OK, INVALID, UNSUPPORTED, CAPACITY, HIP, WORKSPACE = 0, 1, 2, 3, 4, 5
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:moe_status_t|int32_t)\s+(moe_\w+)\s*\(", src, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    L = qm.lib()
+    declared = _declared()
+    assert declared == set(qm.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_header_size_helpers_match_binding():
+    # the binding mirrors the header's static inline size helpers; spot-check the formulas
+    assert qm.cap_tiles(1, 16, 896, 16) == 17
+    assert qm.cap_tiles(16384, 16, 896, 32) == 9088
+    assert qm.cap_tiles(8192, 16, 112, 32) == 4208
+    assert qm.cap_tiles(0, 16, 896, 16) == 0
+
+
+def _layout(cap=100, bm=16, weights=True):
+    return qm.Layout(P.value, P.value if weights else None, P.value, P.value, cap, bm)
+
+
+def _sort(ids=P, w=P, T=4, K=2, eb=0, E=8, layout=None, ws=P, ws_bytes=1 << 20):
+    lay = _layout() if layout is None else layout
+    return qm.lib().moe_sort(ids, w, T, K, eb, E, ctypes.byref(lay), ws, ws_bytes, None)
+
+
+@no_gpu
+def test_sort_validation():
+    assert _sort(T=-1) == INVALID
+    assert _sort(K=0) == INVALID
+    assert _sort(E=0) == INVALID
+    assert _sort(E=4096) == UNSUPPORTED
+    assert _sort(ids=None) == INVALID
+    assert _sort(layout=_layout(bm=64)) == UNSUPPORTED
+    assert _sort(layout=_layout(cap=qm.cap_tiles(4, 2, 8, 16) - 1)) == CAPACITY
+    assert _sort(w=None) == INVALID                     # sorted_weights requested, no topk_w
+    lay = qm.Layout(None, None, P.value, P.value, 100, 16)
+    assert _sort(layout=lay) == INVALID
+    big = 2000
+    assert _sort(T=big, K=16, E=8, layout=_layout(cap=qm.cap_tiles(big, 16, 8, 16)), ws_bytes=16) == WORKSPACE
+
+
+def _fused(a_dtype=0, xs=None, act=0, beta=4.0, lb=25.0, T=4, K=2, E=8, D=256, I=128, layout=None,
+           ws_bytes=1 << 30, out=P, x=P):
+    lay = _layout(cap=qm.cap_tiles(T, K, E, 16)) if layout is None else layout
+    ap = qm.ActParams(act, beta, lb)
+    return qm.lib().moe_fused(x, xs, a_dtype, P, P, P, P, P, ctypes.byref(lay), T, K, E, D, I,
+                              ctypes.byref(ap), out, P, ws_bytes, None)
+
+
+@no_gpu
+def test_fused_validation():
+    assert _fused(a_dtype=7) == INVALID
+    assert _fused(act=5) == UNSUPPORTED                 # unknown activation is rejected
+    assert _fused(beta=0.0) == INVALID                  # no default betas
+    assert _fused(lb=float("nan")) == INVALID
+    assert _fused(D=200) == UNSUPPORTED
+    assert _fused(I=96) == UNSUPPORTED
+    assert _fused(a_dtype=1, xs=None) == INVALID        # fp8 needs scales
+    assert _fused(a_dtype=0, xs=P) == INVALID           # bf16 takes none
+    assert _fused(x=None) == INVALID
+    assert _fused(out=None) == INVALID
+    assert _fused(layout=_layout(cap=1)) == CAPACITY
+    assert _fused(layout=_layout(cap=100, bm=8)) == UNSUPPORTED
+    assert _fused(ws_bytes=10) == WORKSPACE
+    assert _fused(T=0) == OK                            # empty batch: nothing to do
+
+
+@no_gpu
+def test_quant_validation():
+    q = qm.lib().moe_quant_act
+    assert q(P, 4, 64, 0, P, P, None) == INVALID       # bf16 is not a quantized format
+    assert q(P, 4, 48, 1, P, P, None) == INVALID       # cols % 32
+    assert q(P, -1, 64, 1, P, P, None) == INVALID
+    assert q(None, 4, 64, 1, P, P, None) == INVALID
+    assert q(P, 0, 64, 2, P, P, None) == OK             # no rows: nothing to do
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(qm, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(qm, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        qm.lib()
