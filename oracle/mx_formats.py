@@ -114,10 +114,26 @@ def quantize_1x32(v, fmt):
     return codes, (sexp + 127).astype(np.uint8)
 
 
+_E2M1_TABLE = None
+_E4M3_TABLE = None
+
+
+def _value_table(fmt):
+    """Decoded value of every code (the closed forms above, evaluated once per code)."""
+    global _E2M1_TABLE, _E4M3_TABLE
+    if fmt == "e2m1":
+        if _E2M1_TABLE is None:
+            _E2M1_TABLE = e2m1_value(np.arange(16))
+        return _E2M1_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = e4m3_value(np.arange(256))
+    return _E4M3_TABLE
+
+
 def dequantize_1x32(codes, scale_codes, fmt):
     """Inverse of quantize_1x32: element value times 2^(scale - 127), per 32-element block."""
     codes = np.asarray(codes)
-    vals = e2m1_value(codes) if fmt == "e2m1" else e4m3_value(codes)
+    vals = _value_table(fmt)[codes]
     s = e8m0_value(scale_codes)
     blocks = vals.reshape(*vals.shape[:-1], vals.shape[-1] // BLOCK, BLOCK)
     return (blocks * s[..., None]).reshape(vals.shape)
@@ -131,8 +147,8 @@ def pack_fp4(codes):
 
 def unpack_fp4(packed):
     """Split fp4x2 bytes into e2m1 codes: byte i -> elements 2i (low) and 2i + 1 (high)."""
-    packed = np.asarray(packed, dtype=np.int64)
-    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.int64)
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
     out[..., 0::2] = packed & 0xF
     out[..., 1::2] = packed >> 4
     return out
