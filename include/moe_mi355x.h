@@ -56,6 +56,9 @@ typedef enum { MOE_DT_BF16 = 0, MOE_DT_FP8_E4M3 = 1, MOE_DT_FP4_E2M1 = 2 } moe_d
  * (PR 4471 "Technical Details": reject activations other than silu and situv2). */
 typedef enum { MOE_ACT_SITUV2 = 0, MOE_ACT_SILU = 1, MOE_ACT_NONE_TEST = 2 } moe_act_t;
 
+/* Which stages moe_fused runs (see `stages` there). */
+typedef enum { MOE_STAGE_1 = 1, MOE_STAGE_2 = 2, MOE_STAGE_ALL = 3 } moe_stages_t;
+
 /* There are no default betas: PR 4463 "Three tuner defects" item 1 shows two sides silently
  * using different defaults.  beta and linear_beta must be finite and > 0 for SITUV2. */
 typedef struct {
@@ -103,13 +106,14 @@ static inline size_t moe_row_bytes(int32_t cols, int32_t dt) {
   return dt == MOE_DT_BF16 ? (size_t)cols * 2 : dt == MOE_DT_FP8_E4M3 ? (size_t)cols : (size_t)cols / 2;
 }
 
-/* Workspace of moe_fused: an fp32 [T, D] combine accumulator, the stage1 intermediate
- * [cap*bm, I] in a_dtype plus its [cap*bm, I/32] e8m0 scales (fp8/fp4), and for NONE_TEST a
- * fp32 [cap*bm, 2I] debug area holding the raw gate (cols 0..I-1) and up (I..2I-1) sums. */
+/* Workspace of moe_fused, in this order (each part 256-byte aligned): an fp32 [T, D] combine
+ * accumulator, D/16 int32 stage completion counters, the stage1 intermediate [cap*bm, I] in
+ * a_dtype plus its [cap*bm, I/32] e8m0 scales (fp8/fp4), and for NONE_TEST a fp32 [cap*bm, 2I]
+ * debug area holding the raw gate (cols 0..I-1) and up (I..2I-1) sums of each layout row. */
 static inline size_t moe_fused_debug_offset(int32_t tokens, int32_t model_dim, int32_t inter_dim,
                                             int32_t cap_tiles, int32_t block_m, int32_t a_dtype) {
   size_t rows = (size_t)cap_tiles * block_m;
-  return moe_align256((size_t)tokens * model_dim * 4) +
+  return moe_align256((size_t)tokens * model_dim * 4) + moe_align256((size_t)(model_dim / 16) * 4) +
          moe_align256(rows * moe_row_bytes(inter_dim, a_dtype)) +
          moe_align256(a_dtype == MOE_DT_BF16 ? 0 : rows * (size_t)(inter_dim / 32));
 }
@@ -160,6 +164,10 @@ moe_status_t moe_quant_act(const uint16_t *x_bf16, int64_t rows, int64_t cols, i
  *   act       activation and betas (no defaults).
  *   out_bf16  [tokens, D] bf16, overwritten; tokens with no local expert get zeros.
  *   ws        scratch of ws_bytes >= moe_fused_ws_bytes(...).
+ *   stages    MOE_STAGE_ALL (both), MOE_STAGE_1 (Stage1 only: clears the accumulator and
+ *             leaves the intermediate in ws; `out` untouched) or MOE_STAGE_2 (Stage2 + bf16
+ *             finalize only, reading the intermediate a MOE_STAGE_1 call with the same layout
+ *             and shapes left in the same ws).  Any other value -> MOE_ERR_INVALID_ARG.
  * Shapes: D % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED: every K step is one
  * 128-deep block-scaled MFMA); E >= 1.  Stage1 uses fp32 accumulation; the intermediate is
  * stored as bf16 (BF16) or re-encoded with the moe_quant_act rule (FP8, FP4); Stage2
@@ -171,7 +179,8 @@ moe_status_t moe_fused(const void *x, const uint8_t *x_scale, int32_t a_dtype,
                        const float *topk_w, const moe_layout_t *layout,
                        int32_t tokens, int32_t topk, int32_t num_local_experts,
                        int32_t model_dim, int32_t inter_dim, const moe_act_params_t *act,
-                       uint16_t *out_bf16, void *ws, size_t ws_bytes, void *stream);
+                       uint16_t *out_bf16, void *ws, size_t ws_bytes, int32_t stages,
+                       void *stream);
 
 /* The hipError_t value behind the last MOE_ERR_HIP returned on this thread (0 if none). */
 int32_t moe_last_hip_error(void);

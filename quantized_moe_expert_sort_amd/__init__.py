@@ -12,6 +12,7 @@ import torch
 
 DT_BF16, DT_FP8, DT_FP4 = 0, 1, 2
 ACT_SITUV2, ACT_SILU, ACT_NONE_TEST = 0, 1, 2
+STAGE_1, STAGE_2, STAGE_ALL = 1, 2, 3
 DTYPES = {"bf16": DT_BF16, "fp8": DT_FP8, "fp4": DT_FP4}
 ACTS = {"situv2": ACT_SITUV2, "silu": ACT_SILU, "none_test": ACT_NONE_TEST}
 
@@ -58,7 +59,7 @@ def lib():
         L.moe_quant_act.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         L.moe_quant_act.restype = i32
         L.moe_fused.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(Layout), i32, i32, i32,
-                                i32, i32, ctypes.POINTER(ActParams), vp, vp, sz, vp]
+                                i32, i32, ctypes.POINTER(ActParams), vp, vp, sz, i32, vp]
         L.moe_fused.restype = i32
         L.moe_last_hip_error.argtypes = []
         L.moe_last_hip_error.restype = i32
@@ -103,7 +104,8 @@ def row_bytes(cols, dt):
 
 def fused_debug_offset(tokens, model_dim, inter_dim, cap, block_m, a_dtype):
     rows = cap * block_m
-    return (_align256(tokens * model_dim * 4) + _align256(rows * row_bytes(inter_dim, a_dtype))
+    return (_align256(tokens * model_dim * 4) + _align256((model_dim // 16) * 4)
+            + _align256(rows * row_bytes(inter_dim, a_dtype))
             + _align256(0 if a_dtype == DT_BF16 else rows * (inter_dim // 32)))
 
 
@@ -161,9 +163,10 @@ def moe_quant_act(x_bf16, dt, q=None, scale=None):
 
 
 def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, num_local_experts,
-              act="situv2", beta=None, linear_beta=None, out=None, ws=None):
+              act="situv2", beta=None, linear_beta=None, out=None, ws=None, stages=STAGE_ALL):
     """Stage1 + Stage2 over a layout from moe_sort; returns out [T, D] bf16 (or, for
-    act="none_test", the workspace tensor holding the raw gate/up sums)."""
+    act="none_test", the workspace tensor holding the raw gate/up sums).  stages selects
+    STAGE_1, STAGE_2 (reusing the intermediate a STAGE_1 call left in the same ws) or both."""
     d = DTYPES[a_dtype] if isinstance(a_dtype, str) else a_dtype
     a = ACTS[act] if isinstance(act, str) else act
     T, K = topk_w.shape
@@ -180,5 +183,5 @@ def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, n
     _check("moe_fused", lib().moe_fused(_ptr(x), _ptr(x_scale), d, _ptr(w1), _ptr(w1_scale), _ptr(w2),
                                         _ptr(w2_scale), _ptr(topk_w), ctypes.byref(layout.c), T, K,
                                         num_local_experts, D, I, ctypes.byref(params), _ptr(out),
-                                        _ptr(ws), ws.numel(), _stream()))
+                                        _ptr(ws), ws.numel(), stages, _stream()))
     return ws if a == ACT_NONE_TEST else out

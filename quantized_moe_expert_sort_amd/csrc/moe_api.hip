@@ -65,8 +65,9 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
                        const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
                        int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
                        const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       int32_t stages, void* stream) {
   if (!valid_dtype(a_dtype)) return MOE_ERR_INVALID_ARG;
+  if (stages != MOE_STAGE_1 && stages != MOE_STAGE_2 && stages != MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
   if (!act) return MOE_ERR_INVALID_ARG;
   if (act->act != MOE_ACT_SITUV2 && act->act != MOE_ACT_SILU && act->act != MOE_ACT_NONE_TEST)
     return MOE_ERR_UNSUPPORTED;
@@ -84,14 +85,15 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   if (tokens == 0) return MOE_OK;
   if (!x || !w1 || !w1_scale || !w2 || !w2_scale || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
   if ((a_dtype == MOE_DT_BF16) != (x_scale == nullptr)) return MOE_ERR_INVALID_ARG;
-  if (act->act != MOE_ACT_NONE_TEST && !out_bf16) return MOE_ERR_INVALID_ARG;
+  if (act->act != MOE_ACT_NONE_TEST && (stages & MOE_STAGE_2) && !out_bf16) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_fused_ws_bytes(tokens, model_dim, inter_dim, layout->cap_tiles, layout->block_m,
                                     a_dtype, act->act))
     return MOE_ERR_WORKSPACE;
 
   const size_t rows = (size_t)layout->cap_tiles * layout->block_m;
   uint8_t* base = (uint8_t*)ws;
-  const size_t off_inter = moe_align256((size_t)tokens * model_dim * 4);
+  const size_t off_counters = moe_align256((size_t)tokens * model_dim * 4);
+  const size_t off_inter = off_counters + moe_align256((size_t)(model_dim / 16) * 4);
   const size_t off_iscale = off_inter + moe_align256(rows * moe_row_bytes(inter_dim, a_dtype));
   const size_t off_dbg = moe_fused_debug_offset(tokens, model_dim, inter_dim, layout->cap_tiles,
                                                 layout->block_m, a_dtype);
@@ -110,6 +112,8 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   a.inter = base + off_inter;
   a.inter_s = a_dtype == MOE_DT_BF16 ? nullptr : base + off_iscale;
   a.dbg = act->act == MOE_ACT_NONE_TEST ? (float*)(base + off_dbg) : nullptr;
+  a.counters = (int*)(base + off_counters);
+  a.n_counters = 0;
   a.out = out_bf16;
   a.T = tokens;
   a.topk = topk;
@@ -122,6 +126,7 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   a.act = act->act;
   a.beta = act->beta;
   a.linear_beta = act->linear_beta;
+  a.stages = stages;
   return hip_status(moe::launch_fused(a, (hipStream_t)stream));
 }
 

@@ -113,15 +113,29 @@ template <int ADT>
 __host__ __device__ constexpr int row_bytes_den() { return ADT == DT_FP4 ? 2 : 1; }
 
 // ---------------------------------------------------------------- Stage1
+//
+// KW waves split the K steps (step s on wave s % KW); each wave issues the loads of PF of its
+// steps before the first MFMA that uses them, so every lane has PF * (2*NF + MF) 16-byte
+// loads in flight.  The workgroup also clears its slice of the fp32 combine accumulator and
+// of the stage2 completion counters (stage2 runs after this kernel on the same stream).
 
-template <int ADT, int BM, int NI, int ACT>
-__global__ __launch_bounds__(THREADS) void stage1_kernel(FusedArgs p, int n_nblk) {
+template <int ADT, int BM, int NI, int KW, int PF, int MINW, int ACT>
+__global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, int n_nblk) {
+  constexpr int NT = KW * WAVE;
   constexpr int MF = BM / 16;
   constexpr int NF = NI / 16;
   constexpr int NB = 2 * NF;
-  static_assert(ADT == DT_BF16 || (NI % 32 == 0 && (BM * NI) % THREADS == 0),
+  static_assert(ADT == DT_BF16 || (NI % 32 == 0 && (BM * NI) % NT == 0),
                 "a quantized intermediate needs whole 32-column blocks on full waves");
-  __shared__ float red[NWAVES][BM][2 * NI + 1];
+  __shared__ float red[KW][BM][2 * NI + 1];
+
+  if (ACT != ACT_NONE) {
+    const int64_t n4 = (int64_t)p.T * p.D / 4;
+    float4* acc4 = reinterpret_cast<float4*>(p.acc);
+    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT)
+      acc4[i] = float4{0.f, 0.f, 0.f, 0.f};
+    for (int i = blockIdx.x * NT + threadIdx.x; i < p.n_counters; i += gridDim.x * NT) p.counters[i] = 0;
+  }
 
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r16 = lane & 15, g = lane >> 4;
@@ -161,20 +175,37 @@ __global__ __launch_bounds__(THREADS) void stage1_kernel(FusedArgs p, int n_nblk
     for (int j = 0; j < NB; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int S = D / 128;
-  for (int s = wave; s < S; s += NWAVES) {
-    uint4 bq[NB];
-    uint32_t bs[NB];
+  for (int s0 = wave; s0 < S; s0 += KW * PF) {
+    // all weight loads of PF steps first; activations one step ahead of their MFMAs
+    uint4 bq[PF][NB];
+    uint32_t bs[PF][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      bq[j] = ld16(brow[j] + s * 64 + 16 * g);
-      bs[j] = bsrow[j][s * 4 + g];
+    for (int i = 0; i < PF; ++i) {
+      const int s = s0 + i * KW;
+      if (s < S) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          bq[i][j] = ld16(brow[j] + s * 64 + 16 * g);
+          bs[i][j] = bsrow[j][s * 4 + g];
+        }
+      }
     }
+    AOperand<ADT> A[2][MF];
 #pragma unroll
-    for (int f = 0; f < MF; ++f) {
-      AOperand<ADT> A;
-      A.load(arow[f], asrow[f], s, g, aval[f]);
+    for (int f = 0; f < MF; ++f) A[0][f].load(arow[f], asrow[f], s0, g, aval[f]);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[f][j] = A.mma(bq[j], bs[j], acc[f][j]);
+    for (int i = 0; i < PF; ++i) {
+      const int s = s0 + i * KW;
+      if (i + 1 < PF && s + KW < S) {
+#pragma unroll
+        for (int f = 0; f < MF; ++f) A[(i + 1) & 1][f].load(arow[f], asrow[f], s + KW, g, aval[f]);
+      }
+      if (s < S) {
+#pragma unroll
+        for (int f = 0; f < MF; ++f)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[f][j] = A[i & 1][f].mma(bq[i][j], bs[i][j], acc[f][j]);
+      }
     }
   }
 
@@ -187,11 +218,11 @@ __global__ __launch_bounds__(THREADS) void stage1_kernel(FusedArgs p, int n_nblk
   __syncthreads();
 
   const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
-  for (int idx = threadIdx.x; idx < BM * NI; idx += THREADS) {
+  for (int idx = threadIdx.x; idx < BM * NI; idx += NT) {
     const int row = idx / NI, col = idx - row * NI;
     float gs = 0.f, us = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) { gs += red[w][row][col]; us += red[w][row][NI + col]; }
+    for (int w = 0; w < KW; ++w) { gs += red[w][row][col]; us += red[w][row][NI + col]; }
     const int R = tile * BM + row;
     const bool valid = (unsigned)p.sorted_ids[R] < (unsigned)TK;
     const int ocol = nb * NI + col;
@@ -221,15 +252,18 @@ __global__ __launch_bounds__(THREADS) void stage1_kernel(FusedArgs p, int n_nblk
 }
 
 // ---------------------------------------------------------------- Stage2
+//
+// Workgroup (tile, column block nb): blockIdx = nb * cap + tile, so the tiles of one column
+// block run together and share that block's slice of the accumulator rows in L2.
 
-template <int ADT, int BM, int NF>
-__global__ __launch_bounds__(THREADS) void stage2_kernel(FusedArgs p, int n_nblk) {
+template <int ADT, int BM, int NF, int PF, int MINW>
+__global__ __launch_bounds__(THREADS, MINW) void stage2_kernel(FusedArgs p, int cap) {
   constexpr int MF = BM / 16;
   constexpr int NO = NWAVES * NF * 16;
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r16 = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x / n_nblk;
-  const int nb = blockIdx.x - tile * n_nblk;
+  const int tile = blockIdx.x % cap;
+  const int nb = blockIdx.x / cap;
   if (tile >= *p.num_tiles) return;
   const int e = p.expert_ids[tile];
   if (e < 0 || e >= p.E) return;
@@ -255,6 +289,12 @@ __global__ __launch_bounds__(THREADS) void stage2_kernel(FusedArgs p, int n_nblk
     brow[j] = p.w2 + wr * (I / 2);
     bsrow[j] = p.w2s + wr * (I / 32);
   }
+  // rows of this lane's accumulator elements: loaded early, used by the epilogue
+  int vrow[MF][4];
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vrow[f][i] = p.sorted_ids[tile * BM + 16 * f + 4 * g + i];
 
   v4f acc[MF][NF];
 #pragma unroll
@@ -263,45 +303,59 @@ __global__ __launch_bounds__(THREADS) void stage2_kernel(FusedArgs p, int n_nblk
     for (int j = 0; j < NF; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int S = I / 128;
-  for (int s = 0; s < S; ++s) {
-    uint4 bq[NF];
-    uint32_t bs[NF];
+  for (int s0 = 0; s0 < S; s0 += PF) {
+    uint4 bq[PF][NF];
+    uint32_t bs[PF][NF];
 #pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      bq[j] = ld16(brow[j] + s * 64 + 16 * g);
-      bs[j] = bsrow[j][s * 4 + g];
+    for (int i = 0; i < PF; ++i) {
+      if (s0 + i < S) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
+          bs[i][j] = bsrow[j][(s0 + i) * 4 + g];
+        }
+      }
     }
+    AOperand<ADT> A[2][MF];
 #pragma unroll
-    for (int f = 0; f < MF; ++f) {
-      AOperand<ADT> A;
-      A.load(arow[f], asrow[f], s, g, aval[f]);
+    for (int f = 0; f < MF; ++f) A[0][f].load(arow[f], asrow[f], s0, g, aval[f]);
 #pragma unroll
-      for (int j = 0; j < NF; ++j) acc[f][j] = A.mma(bq[j], bs[j], acc[f][j]);
+    for (int i = 0; i < PF; ++i) {
+      if (i + 1 < PF && s0 + i + 1 < S) {
+#pragma unroll
+        for (int f = 0; f < MF; ++f) A[(i + 1) & 1][f].load(arow[f], asrow[f], s0 + i + 1, g, aval[f]);
+      }
+      if (s0 + i < S) {
+#pragma unroll
+        for (int f = 0; f < MF; ++f)
+#pragma unroll
+          for (int j = 0; j < NF; ++j) acc[f][j] = A[i & 1][f].mma(bq[i][j], bs[i][j], acc[f][j]);
+      }
     }
   }
 
+  float wrow[MF][4];
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = vrow[f][i];
+      wrow[f][i] = (unsigned)v < (unsigned)TK ? p.topk_w[v] : 0.f;
+    }
 #pragma unroll
   for (int f = 0; f < MF; ++f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int R = tile * BM + 16 * f + 4 * g + i;
-      const int v = p.sorted_ids[R];
+      const int v = vrow[f][i];
       if ((unsigned)v >= (unsigned)TK) continue;
-      const float w = p.topk_w[v];
       float* orow = p.acc + (size_t)(v / p.topk) * D + nb * NO + wave * NF * 16 + r16;
 #pragma unroll
-      for (int j = 0; j < NF; ++j) unsafeAtomicAdd(orow + 16 * j, acc[f][j][i] * w);
+      for (int j = 0; j < NF; ++j) unsafeAtomicAdd(orow + 16 * j, acc[f][j][i] * wrow[f][i]);
     }
   }
 }
 
-// ---------------------------------------------------------------- zero / finalize
-
-__global__ __launch_bounds__(THREADS) void zero_kernel(float4* __restrict__ a, int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * THREADS;
-  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4; i += stride)
-    a[i] = float4{0.f, 0.f, 0.f, 0.f};
-}
+// ---------------------------------------------------------------- finalize (large batches)
 
 __global__ __launch_bounds__(THREADS) void finalize_kernel(const float4* __restrict__ a, uint2* __restrict__ out,
                                                            int64_t n4) {
@@ -319,23 +373,44 @@ unsigned stream_blocks(int64_t n) {
   return (unsigned)(b < 1 ? 1 : b);
 }
 
+// Stage tiling per activation dtype and block_m.
 template <int ADT, int BM>
-hipError_t run_stages(const FusedArgs& a, hipStream_t s) {
-  constexpr int NI = ADT == DT_BF16 ? 16 : 32;
-  const int n1 = a.I / NI;
+struct Cfg {
+  static constexpr int NI = ADT == DT_BF16 ? 16 : 32;         // intermediate columns / workgroup
+  static constexpr int KW = 4;                                // waves splitting K in stage1
+  static constexpr int PF1 = (ADT == DT_BF16 && BM == 16) ? 8 : 4;   // K steps of weights in flight
+  static constexpr int MINW1 = 2;                               // waves per SIMD kept
+  static constexpr int NF2 = 1;                               // stage2 16-column fragments / wave
+  static constexpr int PF2 = 4;
+  static constexpr int MINW2 = BM == 16 ? 4 : 3;
+};
+
+template <int ADT, int BM>
+hipError_t run_stages(FusedArgs a, hipStream_t s) {
+  using C = Cfg<ADT, BM>;
+  const int n1 = a.I / C::NI;
   const unsigned grid1 = (unsigned)((int64_t)a.cap_tiles * n1);
-  if (a.act == ACT_SITUV2)
-    stage1_kernel<ADT, BM, NI, ACT_SITUV2><<<grid1, THREADS, 0, s>>>(a, n1);
-  else if (a.act == ACT_SILU)
-    stage1_kernel<ADT, BM, NI, ACT_SILU><<<grid1, THREADS, 0, s>>>(a, n1);
-  else
-    stage1_kernel<ADT, BM, NI, ACT_NONE><<<grid1, THREADS, 0, s>>>(a, n1);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.act == ACT_NONE) return err;
-  constexpr int NF = 1;
-  const int n2 = a.D / (NWAVES * NF * 16);
+  const int n2 = a.D / (NWAVES * C::NF2 * 16);
+  a.n_counters = 0;
+  constexpr int T1 = C::KW * WAVE;
+  if (a.stages & 1) {
+    if (a.act == ACT_SITUV2)
+      stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SITUV2><<<grid1, T1, 0, s>>>(a, n1);
+    else if (a.act == ACT_SILU)
+      stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SILU><<<grid1, T1, 0, s>>>(a, n1);
+    else
+      stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_NONE><<<grid1, T1, 0, s>>>(a, n1);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (!(a.stages & 2) || a.act == ACT_NONE) return hipSuccess;
   const unsigned grid2 = (unsigned)((int64_t)a.cap_tiles * n2);
-  stage2_kernel<ADT, BM, NF><<<grid2, THREADS, 0, s>>>(a, n2);
+  stage2_kernel<ADT, BM, C::NF2, C::PF2, C::MINW2><<<grid2, THREADS, 0, s>>>(a, a.cap_tiles);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n4 = (int64_t)a.T * a.D / 4;
+  finalize_kernel<<<stream_blocks(n4), THREADS, 0, s>>>(reinterpret_cast<const float4*>(a.acc),
+                                                        reinterpret_cast<uint2*>(a.out), n4);
   return hipGetLastError();
 }
 
@@ -347,19 +422,9 @@ hipError_t run_dtype(const FusedArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s) {
-  const int64_t n4 = (int64_t)a.T * a.D / 4;
-  if (a.act != ACT_NONE) {
-    zero_kernel<<<stream_blocks(n4), THREADS, 0, s>>>(reinterpret_cast<float4*>(a.acc), n4);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  hipError_t err = a.a_dtype == DT_BF16 ? run_dtype<DT_BF16>(a, s)
-                   : a.a_dtype == DT_FP8 ? run_dtype<DT_FP8>(a, s)
-                                         : run_dtype<DT_FP4>(a, s);
-  if (err != hipSuccess || a.act == ACT_NONE) return err;
-  finalize_kernel<<<stream_blocks(n4), THREADS, 0, s>>>(reinterpret_cast<const float4*>(a.acc),
-                                                        reinterpret_cast<uint2*>(a.out), n4);
-  return hipGetLastError();
+  return a.a_dtype == DT_BF16 ? run_dtype<DT_BF16>(a, s)
+         : a.a_dtype == DT_FP8 ? run_dtype<DT_FP8>(a, s)
+                               : run_dtype<DT_FP4>(a, s);
 }
 
 }  // namespace moe

@@ -39,9 +39,12 @@ struct FusedArgs {
   uint8_t* inter;          // [cap*bm, I] intermediate codes
   uint8_t* inter_s;        // [cap*bm, I/32] intermediate scales (fp8 / fp4)
   float* dbg;              // [cap*bm, 2I] raw gate/up sums (NONE_TEST) or null
+  int* counters;           // [D/16] stage2 completion counters (cleared by stage1)
+  int n_counters;          // counters stage1 clears (set by the launcher)
   uint16_t* out;           // [T, D] bf16
   int T, topk, E, D, I, cap_tiles, block_m, a_dtype, act;
   float beta, linear_beta;
+  int stages;              // bit 0: stage1, bit 1: stage2 + finalize
 };
 
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);

@@ -2,13 +2,16 @@
 // (github ROCm/aiter PR 5118, "Summary": moe_sorting pads every expert up to a full block_m).
 //
 // The layout is unique (experts ascending, rows ascending in v = t*topk + k, sentinel T*topk on
-// padding), so the kernels rank rows without atomics: inside a wave the rank of a row among
-// the lanes holding the same expert comes from per-bit ballots (a match-any), and waves,
-// chunks and experts are combined in index order by exclusive scans.
+// padding), so the kernels rank rows without atomics.  A chunk of CHUNK rows is split into
+// contiguous per-wave sub-chunks; inside a wave the rank of a row among the lanes holding the
+// same expert comes from per-bit ballots (a match-any), each wave keeps its own 16-bit counters
+// in LDS, and an exclusive scan over waves, chunks and experts (in index order) turns the
+// counts into positions.
 //
-//   rows <= MOE_SORT_CHUNK : one workgroup does counting, scan, padding and scatter.
-//   larger                 : count (one workgroup per chunk) -> scan (one workgroup)
-//                            -> scatter (one workgroup per chunk).
+//   rows <= 64    : one wave, ranks and offsets from ballots and cross-lane reads only.
+//   rows <= CHUNK : one workgroup does counting, scan, padding and scatter.
+//   larger        : count (one workgroup per chunk) -> scan (one workgroup)
+//                   -> scatter (one workgroup per chunk).
 #include "moe_kernels.h"
 #include "moe_device.h"
 
@@ -16,16 +19,13 @@ namespace moe {
 
 namespace {
 
-constexpr int SORT_THREADS = 256;
-constexpr int SORT_WAVES = SORT_THREADS / WAVE;
-constexpr int ROWS_PER_WAVE = MOE_SORT_CHUNK / SORT_WAVES;   // 1024
-constexpr int ROUNDS = ROWS_PER_WAVE / WAVE;                  // 16
+constexpr int SORT_THREADS = 512;
+constexpr int SORT_WAVES = SORT_THREADS / WAVE;              // 8
+constexpr int SUB = MOE_SORT_CHUNK / SORT_WAVES;             // rows per wave: 512
+constexpr int ROUNDS = SUB / WAVE;                           // 8
+static_assert(SUB <= 65535, "16-bit per-wave counters");
 
-struct WaveMatch {
-  uint64_t same;   // lanes holding the same key (valid lanes only)
-};
-
-// Lanes of this wave with the same key; key_bits = number of bits that distinguish keys.
+// Lanes of this wave with the same key (valid lanes only); key_bits distinguishes all keys.
 __device__ __forceinline__ uint64_t match_any(int key, bool valid, int key_bits) {
   uint64_t mask = __ballot(valid);
   for (int b = 0; b < key_bits; ++b) {
@@ -42,38 +42,59 @@ __device__ __forceinline__ int bits_for(int n) {   // bits needed to write 0 .. 
   return b;
 }
 
-// Counts the rows of one chunk per (wave, expert) in cnt[w*E + e] and returns, for each of
-// this lane's ROUNDS rows, its rank among the same-expert rows of its wave's sub-chunk.
-__device__ __forceinline__ void count_chunk(const int32_t* __restrict__ ids, int64_t base, int n_in,
-                                            int expert_begin, int E, int* cnt, int key[ROUNDS],
-                                            int rank[ROUNDS]) {
+// Rank the rows [base, base + n_in) of one chunk.  On return (after a barrier):
+//   wc[w*E + e]  exclusive prefix over waves of the rows of expert e (per wave sub-chunk),
+//   tot[e]       rows of expert e in the chunk (if tot != nullptr),
+//   key[r]       local expert of this lane's row in round r (-1 if skipped),
+//   rank[r]      its rank among earlier same-expert rows of the chunk.
+__device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ ids, int64_t base, int n_in,
+                                           int expert_begin, int E, uint16_t* wc, int* tot,
+                                           int key[ROUNDS], int rank[ROUNDS]) {
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  for (int i = threadIdx.x; i < SORT_WAVES * E; i += SORT_THREADS) wc[i] = 0;
+  const int first = w * SUB;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {                 // issue every load before using any
+    const int idx = first + r * WAVE + lane;
+    key[r] = idx < n_in ? ids[base + idx] - expert_begin : -1;
+  }
+  __syncthreads();
   const int kb = bits_for(E);
   const uint64_t lt = (1ull << lane) - 1ull;
-  int* my = cnt + w * E;
+  uint16_t* my = wc + w * E;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    const int idx = w * ROWS_PER_WAVE + r * WAVE + lane;
-    int k = -1;
-    if (idx < n_in) {
-      const int id = ids[base + idx] - expert_begin;
-      k = (id >= 0 && id < E) ? id : -1;
-    }
+    int k = key[r];
+    k = (k >= 0 && k < E) ? k : -1;
+    key[r] = k;
+    rank[r] = 0;
+    if (first + r * WAVE >= n_in) continue;          // uniform: nothing left in this wave
     const bool valid = k >= 0;
     const uint64_t same = match_any(k, valid, kb);
-    int rk = -1;
     if (valid) {
       const int prev = my[k];
-      rk = prev + __popcll(same & lt);
-      if ((same & lt) == 0ull) my[k] = prev + __popcll(same);   // lowest lane of the group
+      rank[r] = prev + __popcll(same & lt);
+      if ((same & lt) == 0ull) my[k] = (uint16_t)(prev + __popcll(same));   // group leader
     }
-    key[r] = k;
-    rank[r] = rk;
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += SORT_THREADS) {
+    int run = 0;
+#pragma unroll
+    for (int ww = 0; ww < SORT_WAVES; ++ww) {
+      const int c = wc[ww * E + e];
+      wc[ww * E + e] = (uint16_t)run;
+      run += c;
+    }
+    if (tot) tot[e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r)
+    if (key[r] >= 0) rank[r] += wc[w * E + key[r]];
 }
 
-// Exclusive scan over a block of SORT_THREADS (or 1024) threads; returns this thread's
-// exclusive prefix and writes the total to *total.
+// Exclusive scan over the NT threads of a block; returns this thread's prefix, *total = sum.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
@@ -85,10 +106,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   }
   if (lane == WAVE - 1) tmp[w] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < NT / WAVE; ++i) { const int t = tmp[i]; tmp[i] = run; run += t; }
-    tmp[NT / WAVE] = run;
+  if (threadIdx.x < WAVE) {
+    const int nw = NT / WAVE;
+    int t = threadIdx.x < nw ? tmp[threadIdx.x] : 0;
+    int s = t;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+      const int o = __shfl_up(s, d, WAVE);
+      if ((int)threadIdx.x >= d) s += o;
+    }
+    if (threadIdx.x < nw) tmp[threadIdx.x] = s - t;
+    if (threadIdx.x == nw - 1) tmp[nw] = s;
   }
   __syncthreads();
   const int res = tmp[w] + incl - v;
@@ -97,7 +125,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return res;
 }
 
-// Per-expert tile counts -> tile offsets, expert_ids, padding sentinels, tail, num_tiles.
+// Per-expert row counts -> tile offsets, expert_ids, padding sentinels, tail, num_tiles.
 // counts[e] holds c_e on entry and the first row position of expert e on exit.
 template <int NT>
 __device__ void layout_from_counts(int* counts, int E, int block_m, int sentinel,
@@ -133,34 +161,77 @@ __device__ void layout_from_counts(int* counts, int E, int block_m, int sentinel
   if (threadIdx.x == 0) *L.num_tiles = total;
 }
 
+// ---------------------------------------------------------------- one-wave path (rows <= 64)
+//
+// Lane i holds row v = i.  Its rank is the number of lower lanes with the same expert; the
+// tile offset of its expert is the sum of the tile counts of the smaller experts present,
+// read from their group leaders (the lowest lane of each expert group).
+
+__global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restrict__ ids,
+                                                         const float* __restrict__ topk_w, int n,
+                                                         int expert_begin, int E, int block_m,
+                                                         SortLayout L) {
+  const int lane = threadIdx.x;
+  int k = -1;
+  if (lane < n) {
+    const int id = ids[lane] - expert_begin;
+    k = (id >= 0 && id < E) ? id : -1;
+  }
+  const bool valid = k >= 0;
+  const uint64_t same = match_any(k, valid, bits_for(E));
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int rank = __popcll(same & lt);
+  const int cnt = __popcll(same);
+  const bool leader = valid && (same & lt) == 0ull;
+  const int tiles = leader ? (cnt + block_m - 1) / block_m : 0;
+  int off = 0, total = 0;
+#pragma unroll 8
+  for (int j = 0; j < WAVE; ++j) {
+    const int kj = __shfl(k, j, WAVE);
+    const int tj = __shfl(tiles, j, WAVE);
+    off += (kj < k) ? tj : 0;
+    total += tj;
+  }
+  const int sentinel = n;
+  if (valid) {
+    const int p = off * block_m + rank;
+    L.sorted_ids[p] = lane;
+    if (L.sorted_w) L.sorted_w[p] = topk_w[lane];
+  }
+  if (leader) {
+    for (int t = 0; t < tiles; ++t) L.expert_ids[off + t] = k;
+    for (int p = cnt; p < tiles * block_m; ++p) {
+      L.sorted_ids[off * block_m + p] = sentinel;
+      if (L.sorted_w) L.sorted_w[off * block_m + p] = 0.0f;
+    }
+  }
+  for (int64_t t = total + lane; t < L.cap_tiles; t += WAVE) L.expert_ids[t] = -1;
+  for (int64_t p = (int64_t)total * block_m + lane; p < (int64_t)L.cap_tiles * block_m; p += WAVE) {
+    L.sorted_ids[p] = sentinel;
+    if (L.sorted_w) L.sorted_w[p] = 0.0f;
+  }
+  if (lane == 0) *L.num_tiles = total;
+}
+
 // ---------------------------------------------------------------- one-workgroup path
 
 __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int n, int expert_begin,
     int E, int block_m, SortLayout L) {
   extern __shared__ int smem[];
-  int* cnt = smem;                       // [SORT_WAVES][E]
-  int* pos = cnt + SORT_WAVES * E;       // [E]
-  int* tmp = pos + E;                    // [SORT_WAVES + 1]
-  for (int i = threadIdx.x; i < SORT_WAVES * E; i += SORT_THREADS) cnt[i] = 0;
-  __syncthreads();
+  int* pos = smem;                                             // [E]
+  int* tmp = pos + E;                                          // [SORT_WAVES + 1]
+  uint16_t* wc = reinterpret_cast<uint16_t*>(tmp + SORT_WAVES + 1);   // [SORT_WAVES][E]
   int key[ROUNDS], rank[ROUNDS];
-  count_chunk(ids, 0, n, expert_begin, E, cnt, key, rank);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += SORT_THREADS) {
-    int run = 0;
-    for (int w = 0; w < SORT_WAVES; ++w) { const int c = cnt[w * E + e]; cnt[w * E + e] = run; run += c; }
-    pos[e] = run;
-  }
-  __syncthreads();
+  rank_chunk(ids, 0, n, expert_begin, E, wc, pos, key, rank);
   layout_from_counts<SORT_THREADS>(pos, E, block_m, n, L, tmp);
   __syncthreads();
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     if (key[r] < 0) continue;
-    const int v = w * ROWS_PER_WAVE + r * WAVE + lane;
-    const int p = pos[key[r]] + cnt[w * E + key[r]] + rank[r];
+    const int v = w * SUB + r * WAVE + lane;
+    const int p = pos[key[r]] + rank[r];
     L.sorted_ids[p] = v;
     if (L.sorted_w) L.sorted_w[p] = topk_w[v];
   }
@@ -171,27 +242,18 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
 __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
     const int32_t* __restrict__ ids, int64_t n, int expert_begin, int E, int* __restrict__ hist,
     int* __restrict__ ranks) {
-  extern __shared__ int cnt[];           // [SORT_WAVES][E]
-  for (int i = threadIdx.x; i < SORT_WAVES * E; i += SORT_THREADS) cnt[i] = 0;
-  __syncthreads();
+  extern __shared__ int smem[];
+  int* tot = smem;                                             // [E]
+  uint16_t* wc = reinterpret_cast<uint16_t*>(tot + E);         // [SORT_WAVES][E]
   const int64_t base = (int64_t)blockIdx.x * MOE_SORT_CHUNK;
   const int n_in = (int)(n - base < MOE_SORT_CHUNK ? n - base : MOE_SORT_CHUNK);
   int key[ROUNDS], rank[ROUNDS];
-  count_chunk(ids, base, n_in, expert_begin, E, cnt, key, rank);
-  __syncthreads();
+  rank_chunk(ids, base, n_in, expert_begin, E, wc, tot, key, rank);
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 #pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    if (key[r] < 0) continue;
-    int before = 0;
-    for (int ww = 0; ww < w; ++ww) before += cnt[ww * E + key[r]];
-    ranks[base + w * ROWS_PER_WAVE + r * WAVE + lane] = before + rank[r];
-  }
-  for (int e = threadIdx.x; e < E; e += SORT_THREADS) {
-    int s = 0;
-    for (int ww = 0; ww < SORT_WAVES; ++ww) s += cnt[ww * E + e];
-    hist[(int64_t)blockIdx.x * E + e] = s;
-  }
+  for (int r = 0; r < ROUNDS; ++r)
+    if (key[r] >= 0) ranks[base + w * SUB + r * WAVE + lane] = rank[r];
+  for (int e = threadIdx.x; e < E; e += SORT_THREADS) hist[(int64_t)blockIdx.x * E + e] = tot[e];
 }
 
 constexpr int SCAN_THREADS = 1024;
@@ -220,11 +282,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void sort_scan_kernel(int* __restrict
   }
 }
 
-__global__ __launch_bounds__(SORT_THREADS) void sort_scatter_kernel(
+__global__ __launch_bounds__(256) void sort_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int64_t n, int expert_begin,
     int E, const int* __restrict__ hist, const int* __restrict__ ranks, SortLayout L) {
   const int64_t base = (int64_t)blockIdx.x * MOE_SORT_CHUNK;
-  for (int i = threadIdx.x; i < MOE_SORT_CHUNK; i += SORT_THREADS) {
+  for (int i = threadIdx.x; i < MOE_SORT_CHUNK; i += 256) {
     const int64_t v = base + i;
     if (v >= n) break;
     const int k = ids[v] - expert_begin;
@@ -240,15 +302,20 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_scatter_kernel(
 hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, int expert_begin,
                        int E, int block_m, const SortLayout& L, void* ws, hipStream_t s) {
   const int sentinel = (int)n;
+  const size_t wc_bytes = (size_t)SORT_WAVES * E * sizeof(uint16_t);
+  if (n <= WAVE) {
+    sort_wave_kernel<<<1, WAVE, 0, s>>>(topk_ids, topk_w, (int)n, expert_begin, E, block_m, L);
+    return hipGetLastError();
+  }
   if (n <= MOE_SORT_CHUNK) {
-    const size_t lds = (size_t)(SORT_WAVES * E + E + SORT_WAVES + 1) * sizeof(int);
+    const size_t lds = (size_t)(E + SORT_WAVES + 1) * sizeof(int) + wc_bytes;
     sort_small_kernel<<<1, SORT_THREADS, lds, s>>>(topk_ids, topk_w, (int)n, expert_begin, E, block_m, L);
     return hipGetLastError();
   }
   const int nchunks = (int)((n + MOE_SORT_CHUNK - 1) / MOE_SORT_CHUNK);
   int* hist = (int*)ws;
   int* ranks = (int*)((char*)ws + moe_align256((size_t)nchunks * E * sizeof(int)));
-  sort_count_kernel<<<nchunks, SORT_THREADS, (size_t)SORT_WAVES * E * sizeof(int), s>>>(
+  sort_count_kernel<<<nchunks, SORT_THREADS, (size_t)E * sizeof(int) + wc_bytes, s>>>(
       topk_ids, n, expert_begin, E, hist, ranks);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -256,7 +323,7 @@ hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, 
       hist, nchunks, E, block_m, sentinel, L);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  sort_scatter_kernel<<<nchunks, SORT_THREADS, 0, s>>>(topk_ids, topk_w, n, expert_begin, E, hist, ranks, L);
+  sort_scatter_kernel<<<nchunks, 256, 0, s>>>(topk_ids, topk_w, n, expert_begin, E, hist, ranks, L);
   return hipGetLastError();
 }
 

@@ -67,11 +67,11 @@ def test_sort_validation():
 
 
 def _fused(a_dtype=0, xs=None, act=0, beta=4.0, lb=25.0, T=4, K=2, E=8, D=256, I=128, layout=None,
-           ws_bytes=1 << 30, out=P, x=P):
+           ws_bytes=1 << 30, out=P, x=P, stages=3):
     lay = _layout(cap=qm.cap_tiles(T, K, E, 16)) if layout is None else layout
     ap = qm.ActParams(act, beta, lb)
     return qm.lib().moe_fused(x, xs, a_dtype, P, P, P, P, P, ctypes.byref(lay), T, K, E, D, I,
-                              ctypes.byref(ap), out, P, ws_bytes, None)
+                              ctypes.byref(ap), out, P, ws_bytes, stages, None)
 
 
 @no_gpu
@@ -89,6 +89,8 @@ def test_fused_validation():
     assert _fused(layout=_layout(cap=1)) == CAPACITY
     assert _fused(layout=_layout(cap=100, bm=8)) == UNSUPPORTED
     assert _fused(ws_bytes=10) == WORKSPACE
+    assert _fused(stages=0) == INVALID
+    assert _fused(stages=4) == INVALID
     assert _fused(T=0) == OK                            # empty batch: nothing to do
 
 
