@@ -68,7 +68,7 @@ class Workbench:
             rows = int(local.sum())
             touched = int(np.unique(ids[local]).size)
             s1 = touched * w1b + wl.tokens * act_bytes(wl.a_dtype, D) + rows * act_bytes(wl.a_dtype, I)
-            s2 = touched * w2b + rows * act_bytes(wl.a_dtype, I) + 2 * wl.tokens * D * 4
+            s2 = touched * w2b + rows * act_bytes(wl.a_dtype, I) + 2 * wl.tokens * D
             self.stats.append({"rows": rows, "touched": touched, "weight_bytes": touched * (w1b + w2b),
                                "flops": 6.0 * rows * D * I, "stage1_bytes": s1, "stage2_bytes": s2})
             x = torch.from_numpy(p["x"].view(np.int16)).cuda()

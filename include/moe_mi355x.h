@@ -71,12 +71,15 @@ typedef struct {
  * Routed row (t, k) is named by its flat index v = t*topk + k.  For each local expert e in
  * ascending order, its rows are listed in ascending v and padded with the sentinel T*topk to a
  * multiple of block_m; experts without rows get no tile.  Tile i holds rows
- * [i*block_m, (i+1)*block_m) of sorted_token_ids and belongs to expert expert_ids[i]. */
+ * [i*block_m, (i+1)*block_m) of sorted_token_ids and belongs to expert expert_ids[i].
+ * row_of is the inverse: the position of routed row v in sorted_token_ids, or -1 when v's
+ * expert is not local. */
 typedef struct {
   int32_t *sorted_token_ids; /* [cap_tiles*block_m] v, or T*topk on padding and unused tiles */
   float *sorted_weights;     /* [cap_tiles*block_m] topk_w[v], 0 on padding; may be NULL */
   int32_t *expert_ids;       /* [cap_tiles] local expert of each tile, -1 past num_tiles */
   int32_t *num_tiles;        /* [1] number of used tiles; written on the device only */
+  int32_t *row_of;           /* [T*topk] position of each routed row, -1 if not local */
   int32_t cap_tiles;         /* tiles the buffers hold, >= moe_cap_tiles(...) */
   int32_t block_m;           /* rows per tile: 16 or 32 */
 } moe_layout_t;
@@ -106,16 +109,23 @@ static inline size_t moe_row_bytes(int32_t cols, int32_t dt) {
   return dt == MOE_DT_BF16 ? (size_t)cols * 2 : dt == MOE_DT_FP8_E4M3 ? (size_t)cols : (size_t)cols / 2;
 }
 
-/* Workspace of moe_fused, in this order (each part 256-byte aligned): an fp32 [T, D] combine
- * accumulator, D/16 int32 stage completion counters, the stage1 intermediate [cap*bm, I] in
- * a_dtype plus its [cap*bm, I/32] e8m0 scales (fp8/fp4), and for NONE_TEST a fp32 [cap*bm, 2I]
- * debug area holding the raw gate (cols 0..I-1) and up (I..2I-1) sums of each layout row. */
+/* Bytes per element of the per-row Stage2 outputs: fp32 for bf16 activations, bf16 otherwise. */
+static inline size_t moe_rowout_elem_bytes(int32_t a_dtype) { return a_dtype == MOE_DT_BF16 ? 4 : 2; }
+
+/* Workspace of moe_fused, in this order (each part 256-byte aligned): the per-row Stage2 outputs
+ * [cap*bm, D] (router weight applied; fp32 or bf16, see moe_rowout_elem_bytes), the stage1
+ * intermediate [cap*bm, I] in a_dtype plus its [cap*bm, I/32] e8m0 scales (fp8/fp4), a
+ * [cap] list of tile groups plus its count (large batches), and for NONE_TEST a fp32
+ * [cap*bm, 2I] debug area holding the raw gate (cols 0..I-1) and up (I..2I-1) sums of each
+ * layout row. */
 static inline size_t moe_fused_debug_offset(int32_t tokens, int32_t model_dim, int32_t inter_dim,
                                             int32_t cap_tiles, int32_t block_m, int32_t a_dtype) {
   size_t rows = (size_t)cap_tiles * block_m;
-  return moe_align256((size_t)tokens * model_dim * 4) + moe_align256((size_t)(model_dim / 16) * 4) +
+  (void)tokens;
+  return moe_align256(rows * (size_t)model_dim * moe_rowout_elem_bytes(a_dtype)) +
          moe_align256(rows * moe_row_bytes(inter_dim, a_dtype)) +
-         moe_align256(a_dtype == MOE_DT_BF16 ? 0 : rows * (size_t)(inter_dim / 32));
+         moe_align256(a_dtype == MOE_DT_BF16 ? 0 : rows * (size_t)(inter_dim / 32)) +
+         moe_align256((size_t)cap_tiles * 8) + 256;
 }
 
 static inline size_t moe_fused_ws_bytes(int32_t tokens, int32_t model_dim, int32_t inter_dim,
@@ -132,7 +142,8 @@ static inline size_t moe_fused_ws_bytes(int32_t tokens, int32_t model_dim, int32
  *   topk_w    [tokens, topk] fp32 router weights, or NULL; required iff
  *             layout->sorted_weights is non-NULL.
  *   layout    buffers to fill; cap_tiles >= moe_cap_tiles(tokens, topk, num_local_experts,
- *             block_m), block_m in {16, 32}.  Every entry of all four buffers is written.
+ *             block_m), block_m in {16, 32}.  Every entry of all buffers is written (row_of may
+ *             be NULL here; moe_fused needs it).
  *   ws        device scratch of ws_bytes >= moe_sort_ws_bytes(tokens, topk, num_local_experts).
  * The result is unique and bit-exact: it does not depend on launch order or timing.
  * Limits: 1 <= tokens*topk < 2^31, 1 <= num_local_experts <= 8192. */
@@ -171,8 +182,9 @@ moe_status_t moe_quant_act(const uint16_t *x_bf16, int64_t rows, int64_t cols, i
  * Shapes: D % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED: every K step is one
  * 128-deep block-scaled MFMA); E >= 1.  Stage1 uses fp32 accumulation; the intermediate is
  * stored as bf16 (BF16) or re-encoded with the moe_quant_act rule (FP8, FP4); Stage2
- * accumulates in fp32 and the per-token sum uses fp32 atomics, so the last bits of `out` may
- * differ from run to run. */
+ * accumulates in fp32, stores each routed row's weighted output (fp32 for BF16, bf16
+ * otherwise), and a gather kernel sums each token's rows in ascending k in fp32 and rounds to
+ * bf16: the result is deterministic.  layout->row_of must be set. */
 moe_status_t moe_fused(const void *x, const uint8_t *x_scale, int32_t a_dtype,
                        const uint8_t *w1, const uint8_t *w1_scale,
                        const uint8_t *w2, const uint8_t *w2_scale,

@@ -94,7 +94,8 @@ def sort_layout(topk_ids, expert_begin, num_local_experts, block_m, topk_w=None,
 
     Returns dict with sorted_token_ids [cap*bm] int32 (flat index v = t*topk + k, sentinel
     T*topk), sorted_weights [cap*bm] float32 (0 on padding), expert_ids [cap] int32 (local
-    expert index, -1 past num_tiles), num_tiles int, counts [E] int."""
+    expert index, -1 past num_tiles), row_of [T*topk] int32 (position of row v in
+    sorted_token_ids, -1 if its expert is not local), num_tiles int, counts [E] int."""
     topk_ids = np.asarray(topk_ids)
     T, K = topk_ids.shape
     flat = topk_ids.reshape(-1)
@@ -121,7 +122,11 @@ def sort_layout(topk_ids, expert_begin, num_local_experts, block_m, topk_w=None,
             wts[start:start + len(vs)] = wflat[vs]
         eids[tile:tile + ntile] = e
         tile += ntile
-    return {"sorted_token_ids": ids, "sorted_weights": wts, "expert_ids": eids,
+    row_of = np.full(T * K, -1, dtype=np.int32)
+    for pos in range(tile * block_m):
+        if ids[pos] != sentinel:
+            row_of[ids[pos]] = pos
+    return {"sorted_token_ids": ids, "sorted_weights": wts, "expert_ids": eids, "row_of": row_of,
             "num_tiles": tile, "counts": counts, "cap": cap}
 
 

@@ -36,7 +36,7 @@ class MoeError(RuntimeError):
 class Layout(ctypes.Structure):
     _fields_ = [("sorted_token_ids", ctypes.c_void_p), ("sorted_weights", ctypes.c_void_p),
                 ("expert_ids", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p),
-                ("cap_tiles", ctypes.c_int32), ("block_m", ctypes.c_int32)]
+                ("row_of", ctypes.c_void_p), ("cap_tiles", ctypes.c_int32), ("block_m", ctypes.c_int32)]
 
 
 class ActParams(ctypes.Structure):
@@ -102,11 +102,16 @@ def row_bytes(cols, dt):
     return cols * 2 if dt == DT_BF16 else cols if dt == DT_FP8 else cols // 2
 
 
+def rowout_elem_bytes(a_dtype):
+    return 4 if a_dtype == DT_BF16 else 2
+
+
 def fused_debug_offset(tokens, model_dim, inter_dim, cap, block_m, a_dtype):
     rows = cap * block_m
-    return (_align256(tokens * model_dim * 4) + _align256((model_dim // 16) * 4)
+    return (_align256(rows * model_dim * rowout_elem_bytes(a_dtype))
             + _align256(rows * row_bytes(inter_dim, a_dtype))
-            + _align256(0 if a_dtype == DT_BF16 else rows * (inter_dim // 32)))
+            + _align256(0 if a_dtype == DT_BF16 else rows * (inter_dim // 32))
+            + _align256(cap * 8) + 256)
 
 
 def fused_ws_bytes(tokens, model_dim, inter_dim, cap, block_m, a_dtype, act):
@@ -130,9 +135,11 @@ class MoeLayout:
         self.sorted_weights = torch.empty(n, dtype=torch.float32, device=device) if with_weights else None
         self.expert_ids = torch.empty(max(self.cap, 1), dtype=torch.int32, device=device)
         self.num_tiles = torch.empty(1, dtype=torch.int32, device=device)
+        self.row_of = torch.empty(max(tokens * topk, 1), dtype=torch.int32, device=device)
         self.c = Layout(self.sorted_token_ids.data_ptr(),
                         None if self.sorted_weights is None else self.sorted_weights.data_ptr(),
-                        self.expert_ids.data_ptr(), self.num_tiles.data_ptr(), self.cap, block_m)
+                        self.expert_ids.data_ptr(), self.num_tiles.data_ptr(), self.row_of.data_ptr(),
+                        self.cap, block_m)
 
 
 def moe_sort(topk_ids, topk_w, expert_begin, num_local_experts, block_m, with_weights=True,

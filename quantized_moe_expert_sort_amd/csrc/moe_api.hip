@@ -46,7 +46,7 @@ moe_status_t moe_sort(const int32_t* topk_ids, const float* topk_w, int32_t toke
     if (ws_bytes < moe_sort_ws_bytes(tokens, topk, num_local_experts)) return MOE_ERR_WORKSPACE;
   }
   moe::SortLayout L{layout->sorted_token_ids, layout->sorted_weights, layout->expert_ids,
-                    layout->num_tiles, layout->cap_tiles};
+                    layout->num_tiles, layout->row_of, layout->cap_tiles};
   return hip_status(moe::launch_sort(topk_ids, topk_w, n, expert_begin, num_local_experts,
                                      layout->block_m, L, ws, (hipStream_t)stream));
 }
@@ -85,16 +85,18 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   if (tokens == 0) return MOE_OK;
   if (!x || !w1 || !w1_scale || !w2 || !w2_scale || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
   if ((a_dtype == MOE_DT_BF16) != (x_scale == nullptr)) return MOE_ERR_INVALID_ARG;
-  if (act->act != MOE_ACT_NONE_TEST && (stages & MOE_STAGE_2) && !out_bf16) return MOE_ERR_INVALID_ARG;
+  if (act->act != MOE_ACT_NONE_TEST && (stages & MOE_STAGE_2) && (!out_bf16 || !layout->row_of))
+    return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe_fused_ws_bytes(tokens, model_dim, inter_dim, layout->cap_tiles, layout->block_m,
                                     a_dtype, act->act))
     return MOE_ERR_WORKSPACE;
 
   const size_t rows = (size_t)layout->cap_tiles * layout->block_m;
   uint8_t* base = (uint8_t*)ws;
-  const size_t off_counters = moe_align256((size_t)tokens * model_dim * 4);
-  const size_t off_inter = off_counters + moe_align256((size_t)(model_dim / 16) * 4);
+  const size_t off_inter = moe_align256(rows * (size_t)model_dim * moe_rowout_elem_bytes(a_dtype));
   const size_t off_iscale = off_inter + moe_align256(rows * moe_row_bytes(inter_dim, a_dtype));
+  const size_t off_groups = off_iscale + moe_align256(a_dtype == MOE_DT_BF16 ? 0 : rows * (size_t)(inter_dim / 32));
+  const size_t off_ngroups = off_groups + moe_align256((size_t)layout->cap_tiles * 8);
   const size_t off_dbg = moe_fused_debug_offset(tokens, model_dim, inter_dim, layout->cap_tiles,
                                                 layout->block_m, a_dtype);
   moe::FusedArgs a;
@@ -108,12 +110,13 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   a.sorted_ids = layout->sorted_token_ids;
   a.expert_ids = layout->expert_ids;
   a.num_tiles = layout->num_tiles;
-  a.acc = (float*)base;
+  a.rowout = base;
+  a.groups = (int2*)(base + off_groups);
+  a.num_groups = (int32_t*)(base + off_ngroups);
+  a.row_of = layout->row_of;
   a.inter = base + off_inter;
   a.inter_s = a_dtype == MOE_DT_BF16 ? nullptr : base + off_iscale;
   a.dbg = act->act == MOE_ACT_NONE_TEST ? (float*)(base + off_dbg) : nullptr;
-  a.counters = (int*)(base + off_counters);
-  a.n_counters = 0;
   a.out = out_bf16;
   a.T = tokens;
   a.topk = topk;

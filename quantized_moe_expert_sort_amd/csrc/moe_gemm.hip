@@ -12,8 +12,8 @@
 // Stage2 (PR 5118 review items 9-10 and commit notes: bf16 x MXFP4 stage2, atomic scatter):
 //   one workgroup = one tile x 64 * NF output columns; each wave owns 16 * NF columns over the
 //   whole K = inter_dim.  The fp32 result row is scaled by the router weight of its routed row
-//   and added with fp32 atomics into the token's row of the accumulator.
-// Finalize rounds the fp32 accumulator to bf16.
+//   and stored as that routed row's output (fp32 for bf16 activations, bf16 otherwise).
+// Combine sums each token's routed-row outputs (via the sort's inverse map) and rounds to bf16.
 #include "moe_kernels.h"
 #include "moe_device.h"
 
@@ -114,10 +114,9 @@ __host__ __device__ constexpr int row_bytes_den() { return ADT == DT_FP4 ? 2 : 1
 
 // ---------------------------------------------------------------- Stage1
 //
-// KW waves split the K steps (step s on wave s % KW); each wave issues the loads of PF of its
-// steps before the first MFMA that uses them, so every lane has PF * (2*NF + MF) 16-byte
-// loads in flight.  The workgroup also clears its slice of the fp32 combine accumulator and
-// of the stage2 completion counters (stage2 runs after this kernel on the same stream).
+// KW waves split the K steps (each wave a contiguous range); each wave issues the weight and
+// activation loads of PF of its steps before the first MFMA that uses them, so every lane has
+// PF * (2*NF + MF) loads in flight and waits once per PF steps.
 
 template <int ADT, int BM, int NI, int KW, int PF, int MINW, int ACT>
 __global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, int n_nblk) {
@@ -128,14 +127,6 @@ __global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, in
   static_assert(ADT == DT_BF16 || (NI % 32 == 0 && (BM * NI) % NT == 0),
                 "a quantized intermediate needs whole 32-column blocks on full waves");
   __shared__ float red[KW][BM][2 * NI + 1];
-
-  if (ACT != ACT_NONE) {
-    const int64_t n4 = (int64_t)p.T * p.D / 4;
-    float4* acc4 = reinterpret_cast<float4*>(p.acc);
-    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT)
-      acc4[i] = float4{0.f, 0.f, 0.f, 0.f};
-    for (int i = blockIdx.x * NT + threadIdx.x; i < p.n_counters; i += gridDim.x * NT) p.counters[i] = 0;
-  }
 
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r16 = lane & 15, g = lane >> 4;
@@ -174,37 +165,38 @@ __global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, in
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // wave `wave` owns the contiguous K steps [k_lo, k_hi); all loads of PF steps are issued
+  // before the first MFMA that uses them
   const int S = D / 128;
-  for (int s0 = wave; s0 < S; s0 += KW * PF) {
-    // all weight loads of PF steps first; activations one step ahead of their MFMAs
+  const int spw = (S + KW - 1) / KW;
+  const int k_lo = wave * spw, k_hi = min(S, k_lo + spw);
+  for (int s0 = k_lo; s0 < k_hi; s0 += PF) {
     uint4 bq[PF][NB];
     uint32_t bs[PF][NB];
+    AOperand<ADT> A[PF][MF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int s = s0 + i * KW;
-      if (s < S) {
+      if (s0 + i < k_hi) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          bq[i][j] = ld16(brow[j] + s * 64 + 16 * g);
-          bs[i][j] = bsrow[j][s * 4 + g];
+          bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
+          bs[i][j] = bsrow[j][(s0 + i) * 4 + g];
         }
       }
     }
-    AOperand<ADT> A[2][MF];
 #pragma unroll
-    for (int f = 0; f < MF; ++f) A[0][f].load(arow[f], asrow[f], s0, g, aval[f]);
+    for (int i = 0; i < PF; ++i)
+      if (s0 + i < k_hi) {
+#pragma unroll
+        for (int f = 0; f < MF; ++f) A[i][f].load(arow[f], asrow[f], s0 + i, g, aval[f]);
+      }
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int s = s0 + i * KW;
-      if (i + 1 < PF && s + KW < S) {
-#pragma unroll
-        for (int f = 0; f < MF; ++f) A[(i + 1) & 1][f].load(arow[f], asrow[f], s + KW, g, aval[f]);
-      }
-      if (s < S) {
+      if (s0 + i < k_hi) {
 #pragma unroll
         for (int f = 0; f < MF; ++f)
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[f][j] = A[i & 1][f].mma(bq[i][j], bs[i][j], acc[f][j]);
+          for (int j = 0; j < NB; ++j) acc[f][j] = A[i][f].mma(bq[i][j], bs[i][j], acc[f][j]);
       }
     }
   }
@@ -316,20 +308,20 @@ __global__ __launch_bounds__(THREADS, MINW) void stage2_kernel(FusedArgs p, int 
         }
       }
     }
-    AOperand<ADT> A[2][MF];
+    AOperand<ADT> A[PF][MF];
 #pragma unroll
-    for (int f = 0; f < MF; ++f) A[0][f].load(arow[f], asrow[f], s0, g, aval[f]);
+    for (int i = 0; i < PF; ++i)
+      if (s0 + i < S) {
+#pragma unroll
+        for (int f = 0; f < MF; ++f) A[i][f].load(arow[f], asrow[f], s0 + i, g, aval[f]);
+      }
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      if (i + 1 < PF && s0 + i + 1 < S) {
-#pragma unroll
-        for (int f = 0; f < MF; ++f) A[(i + 1) & 1][f].load(arow[f], asrow[f], s0 + i + 1, g, aval[f]);
-      }
       if (s0 + i < S) {
 #pragma unroll
         for (int f = 0; f < MF; ++f)
 #pragma unroll
-          for (int j = 0; j < NF; ++j) acc[f][j] = A[i & 1][f].mma(bq[i][j], bs[i][j], acc[f][j]);
+          for (int j = 0; j < NF; ++j) acc[f][j] = A[i][f].mma(bq[i][j], bs[i][j], acc[f][j]);
       }
     }
   }
@@ -342,29 +334,86 @@ __global__ __launch_bounds__(THREADS, MINW) void stage2_kernel(FusedArgs p, int 
       const int v = vrow[f][i];
       wrow[f][i] = (unsigned)v < (unsigned)TK ? p.topk_w[v] : 0.f;
     }
+  // each routed row's weighted output goes to its own row of rowout (no atomics); padding rows
+  // are not written and never read
 #pragma unroll
   for (int f = 0; f < MF; ++f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int v = vrow[f][i];
-      if ((unsigned)v >= (unsigned)TK) continue;
-      float* orow = p.acc + (size_t)(v / p.topk) * D + nb * NO + wave * NF * 16 + r16;
+      if ((unsigned)vrow[f][i] >= (unsigned)TK) continue;
+      const size_t R = (size_t)tile * BM + 16 * f + 4 * g + i;
+      const size_t c0 = (size_t)nb * NO + wave * NF * 16 + r16;
 #pragma unroll
-      for (int j = 0; j < NF; ++j) unsafeAtomicAdd(orow + 16 * j, acc[f][j][i] * wrow[f][i]);
+      for (int j = 0; j < NF; ++j) {
+        const float o = acc[f][j][i] * wrow[f][i];
+        if (ADT == DT_BF16) reinterpret_cast<float*>(p.rowout)[R * D + c0 + 16 * j] = o;
+        else reinterpret_cast<uint16_t*>(p.rowout)[R * D + c0 + 16 * j] = f32_to_bf16_rne(o);
+      }
     }
   }
 }
 
-// ---------------------------------------------------------------- finalize (large batches)
+// ---------------------------------------------------------------- combine
+//
+// out[t, c] = sum over k (ascending) of rowout[row_of[t*topk + k], c], in fp32, rounded to
+// bf16.  Thread = 8 consecutive columns of one token; rows of non-local experts (-1) are skipped.
 
-__global__ __launch_bounds__(THREADS) void finalize_kernel(const float4* __restrict__ a, uint2* __restrict__ out,
-                                                           int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * THREADS;
-  for (int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x; i < n4; i += stride) {
-    const float4 v = a[i];
-    out[i] = uint2{(uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16),
-                   (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16)};
+template <bool F32>
+__global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restrict__ rowout,
+                                                          const int32_t* __restrict__ row_of,
+                                                          uint16_t* __restrict__ out, int T, int topk,
+                                                          int D) {
+  const int groups = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+  if (idx >= (int64_t)T * groups) return;
+  const int t = (int)(idx / groups), c = (int)(idx - (int64_t)t * groups) * 8;
+  float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // all row indices of a group of KG slots first, then all their row loads, then the sums
+  constexpr int KG = 8;
+  for (int k0 = 0; k0 < topk; k0 += KG) {
+    int r[KG];
+#pragma unroll
+    for (int u = 0; u < KG; ++u) r[u] = k0 + u < topk ? row_of[(int64_t)t * topk + k0 + u] : -1;
+    if (F32) {
+      float4 a[KG], b[KG];
+#pragma unroll
+      for (int u = 0; u < KG; ++u) {
+        if (r[u] >= 0) {
+          const float4* src = reinterpret_cast<const float4*>(rowout + ((size_t)r[u] * D + c) * 4);
+          a[u] = src[0];
+          b[u] = src[1];
+        } else {
+          a[u] = b[u] = float4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KG; ++u) {
+        sum[0] += a[u].x; sum[1] += a[u].y; sum[2] += a[u].z; sum[3] += a[u].w;
+        sum[4] += b[u].x; sum[5] += b[u].y; sum[6] += b[u].z; sum[7] += b[u].w;
+      }
+    } else {
+      uint4 q[KG];
+#pragma unroll
+      for (int u = 0; u < KG; ++u)
+        q[u] = r[u] >= 0 ? *reinterpret_cast<const uint4*>(rowout + ((size_t)r[u] * D + c) * 2)
+                         : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < KG; ++u) {
+        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          sum[2 * h] += __uint_as_float(w[h] << 16);
+          sum[2 * h + 1] += __uint_as_float(w[h] & 0xFFFF0000u);
+        }
+      }
+    }
   }
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16_rne(sum[0]) | ((uint32_t)f32_to_bf16_rne(sum[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16_rne(sum[2]) | ((uint32_t)f32_to_bf16_rne(sum[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16_rne(sum[4]) | ((uint32_t)f32_to_bf16_rne(sum[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16_rne(sum[6]) | ((uint32_t)f32_to_bf16_rne(sum[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * D + c) = o;
 }
 
 unsigned stream_blocks(int64_t n) {
@@ -378,11 +427,11 @@ template <int ADT, int BM>
 struct Cfg {
   static constexpr int NI = ADT == DT_BF16 ? 16 : 32;         // intermediate columns / workgroup
   static constexpr int KW = 4;                                // waves splitting K in stage1
-  static constexpr int PF1 = (ADT == DT_BF16 && BM == 16) ? 8 : 4;   // K steps of weights in flight
+  static constexpr int PF1 = (ADT == DT_BF16 && BM == 16) ? 7 : 4;   // K steps in flight per wave
   static constexpr int MINW1 = 2;                               // waves per SIMD kept
   static constexpr int NF2 = 1;                               // stage2 16-column fragments / wave
   static constexpr int PF2 = 4;
-  static constexpr int MINW2 = BM == 16 ? 4 : 3;
+  static constexpr int MINW2 = BM == 16 ? 4 : 2;
 };
 
 template <int ADT, int BM>
@@ -391,9 +440,11 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
   const int n1 = a.I / C::NI;
   const unsigned grid1 = (unsigned)((int64_t)a.cap_tiles * n1);
   const int n2 = a.D / (NWAVES * C::NF2 * 16);
-  a.n_counters = 0;
   constexpr int T1 = C::KW * WAVE;
-  if (a.stages & 1) {
+  if (ADT != DT_BF16 && a.T >= TILED_MIN_TOKENS && tiled_path_supported(a)) {
+    hipError_t err = launch_tiled(a, a.groups, a.num_groups, s);
+    if (err != hipSuccess || !(a.stages & 2)) return err;
+  } else if (a.stages & 1) {
     if (a.act == ACT_SITUV2)
       stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SITUV2><<<grid1, T1, 0, s>>>(a, n1);
     else if (a.act == ACT_SILU)
@@ -404,13 +455,18 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   if (!(a.stages & 2) || a.act == ACT_NONE) return hipSuccess;
-  const unsigned grid2 = (unsigned)((int64_t)a.cap_tiles * n2);
-  stage2_kernel<ADT, BM, C::NF2, C::PF2, C::MINW2><<<grid2, THREADS, 0, s>>>(a, a.cap_tiles);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int64_t n4 = (int64_t)a.T * a.D / 4;
-  finalize_kernel<<<stream_blocks(n4), THREADS, 0, s>>>(reinterpret_cast<const float4*>(a.acc),
-                                                        reinterpret_cast<uint2*>(a.out), n4);
+  if (!(ADT != DT_BF16 && a.T >= TILED_MIN_TOKENS && tiled_path_supported(a))) {
+    const unsigned grid2 = (unsigned)((int64_t)a.cap_tiles * n2);
+    stage2_kernel<ADT, BM, C::NF2, C::PF2, C::MINW2><<<grid2, THREADS, 0, s>>>(a, a.cap_tiles);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int64_t nthreads = (int64_t)a.T * (a.D / 8);
+  const unsigned gridc = (unsigned)((nthreads + THREADS - 1) / THREADS);
+  if (ADT == DT_BF16)
+    combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
+  else
+    combine_kernel<false><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
   return hipGetLastError();
 }
 

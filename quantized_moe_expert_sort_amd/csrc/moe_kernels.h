@@ -13,6 +13,7 @@ struct SortLayout {
   float* sorted_w;        // may be null
   int32_t* expert_ids;
   int32_t* num_tiles;
+  int32_t* row_of;        // may be null
   int64_t cap_tiles;
 };
 
@@ -35,12 +36,13 @@ struct FusedArgs {
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* num_tiles;
-  float* acc;              // [T, D] fp32 combine accumulator
+  const int32_t* row_of;   // [T*topk] position of each routed row or -1
+  uint8_t* rowout;         // [cap*bm, D] weighted stage2 rows (fp32 for bf16 activations, else bf16)
   uint8_t* inter;          // [cap*bm, I] intermediate codes
   uint8_t* inter_s;        // [cap*bm, I/32] intermediate scales (fp8 / fp4)
+  int2* groups;            // [cap] tile groups (large-batch path)
+  int32_t* num_groups;     // [1]
   float* dbg;              // [cap*bm, 2I] raw gate/up sums (NONE_TEST) or null
-  int* counters;           // [D/16] stage2 completion counters (cleared by stage1)
-  int n_counters;          // counters stage1 clears (set by the launcher)
   uint16_t* out;           // [T, D] bf16
   int T, topk, E, D, I, cap_tiles, block_m, a_dtype, act;
   float beta, linear_beta;
@@ -48,5 +50,10 @@ struct FusedArgs {
 };
 
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
+
+// Large-batch stages (moe_gemm_tiled.hip): tile groups of one expert, LDS-tiled GEMMs.
+bool tiled_path_supported(const FusedArgs& a);
+hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipStream_t s);
+constexpr int TILED_MIN_TOKENS = 2048;
 
 }  // namespace moe

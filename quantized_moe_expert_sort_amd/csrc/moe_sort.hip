@@ -187,17 +187,18 @@ __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restri
   int off = 0, total = 0;
 #pragma unroll 8
   for (int j = 0; j < WAVE; ++j) {
-    const int kj = __shfl(k, j, WAVE);
-    const int tj = __shfl(tiles, j, WAVE);
+    const int kj = __builtin_amdgcn_readlane(k, j);
+    const int tj = __builtin_amdgcn_readlane(tiles, j);
     off += (kj < k) ? tj : 0;
     total += tj;
   }
   const int sentinel = n;
+  const int p = off * block_m + rank;
   if (valid) {
-    const int p = off * block_m + rank;
     L.sorted_ids[p] = lane;
     if (L.sorted_w) L.sorted_w[p] = topk_w[lane];
   }
+  if (L.row_of && lane < n) L.row_of[lane] = valid ? p : -1;
   if (leader) {
     for (int t = 0; t < tiles; ++t) L.expert_ids[off + t] = k;
     for (int p = cnt; p < tiles * block_m; ++p) {
@@ -229,11 +230,15 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    if (key[r] < 0) continue;
     const int v = w * SUB + r * WAVE + lane;
+    if (key[r] < 0) {
+      if (L.row_of && v < n) L.row_of[v] = -1;
+      continue;
+    }
     const int p = pos[key[r]] + rank[r];
     L.sorted_ids[p] = v;
     if (L.sorted_w) L.sorted_w[p] = topk_w[v];
+    if (L.row_of) L.row_of[v] = p;
   }
 }
 
@@ -290,10 +295,14 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(
     const int64_t v = base + i;
     if (v >= n) break;
     const int k = ids[v] - expert_begin;
-    if (k < 0 || k >= E) continue;
+    if (k < 0 || k >= E) {
+      if (L.row_of) L.row_of[v] = -1;
+      continue;
+    }
     const int p = hist[(int64_t)blockIdx.x * E + k] + ranks[v];
     L.sorted_ids[p] = (int32_t)v;
     if (L.sorted_w) L.sorted_w[p] = topk_w[v];
+    if (L.row_of) L.row_of[v] = p;
   }
 }
 

@@ -41,8 +41,8 @@ def test_header_size_helpers_match_binding():
     assert qm.cap_tiles(0, 16, 896, 16) == 0
 
 
-def _layout(cap=100, bm=16, weights=True):
-    return qm.Layout(P.value, P.value if weights else None, P.value, P.value, cap, bm)
+def _layout(cap=100, bm=16, weights=True, row_of=True):
+    return qm.Layout(P.value, P.value if weights else None, P.value, P.value, P.value if row_of else None, cap, bm)
 
 
 def _sort(ids=P, w=P, T=4, K=2, eb=0, E=8, layout=None, ws=P, ws_bytes=1 << 20):
@@ -60,7 +60,7 @@ def test_sort_validation():
     assert _sort(layout=_layout(bm=64)) == UNSUPPORTED
     assert _sort(layout=_layout(cap=qm.cap_tiles(4, 2, 8, 16) - 1)) == CAPACITY
     assert _sort(w=None) == INVALID                     # sorted_weights requested, no topk_w
-    lay = qm.Layout(None, None, P.value, P.value, 100, 16)
+    lay = qm.Layout(None, None, P.value, P.value, P.value, 100, 16)
     assert _sort(layout=lay) == INVALID
     big = 2000
     assert _sort(T=big, K=16, E=8, layout=_layout(cap=qm.cap_tiles(big, 16, 8, 16)), ws_bytes=16) == WORKSPACE
@@ -89,6 +89,7 @@ def test_fused_validation():
     assert _fused(layout=_layout(cap=1)) == CAPACITY
     assert _fused(layout=_layout(cap=100, bm=8)) == UNSUPPORTED
     assert _fused(ws_bytes=10) == WORKSPACE
+    assert _fused(layout=_layout(cap=100, row_of=False)) == INVALID   # the combine needs row_of
     assert _fused(stages=0) == INVALID
     assert _fused(stages=4) == INVALID
     assert _fused(T=0) == OK                            # empty batch: nothing to do

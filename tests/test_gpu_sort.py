@@ -20,7 +20,8 @@ def gpu_layout(ids, w, eb, E, bm, with_weights=True):
     return {"sorted_token_ids": lay.sorted_token_ids.cpu().numpy()[:n],
             "sorted_weights": None if not with_weights else lay.sorted_weights.cpu().numpy()[:n],
             "expert_ids": lay.expert_ids.cpu().numpy()[:lay.cap],
-            "num_tiles": int(lay.num_tiles.cpu().item()), "cap": lay.cap}
+            "num_tiles": int(lay.num_tiles.cpu().item()), "cap": lay.cap,
+            "row_of": lay.row_of.cpu().numpy()[:ids.size]}
 
 
 def check_sort(ids, w, eb, E, bm, with_weights=True):
@@ -30,6 +31,7 @@ def check_sort(ids, w, eb, E, bm, with_weights=True):
     assert got["num_tiles"] == ref["num_tiles"]
     assert np.array_equal(got["expert_ids"], ref["expert_ids"])
     assert np.array_equal(got["sorted_token_ids"], ref["sorted_token_ids"])
+    assert np.array_equal(got["row_of"], ref["row_of"])
     if with_weights:
         assert np.array_equal(got["sorted_weights"].view(np.uint32), ref["sorted_weights"].view(np.uint32))
     return ref

@@ -123,6 +123,12 @@ def test_sort_layout_brute_force(T, K, E, eb, nloc, bm):
     assert int(np.sum(-(-c // bm) * bm - c)) == int(np.sum(s[:nt * bm] == T * K))
     assert np.all(np.diff(lay["expert_ids"][:nt]) >= 0)
     assert lay["cap"] >= nt
+    # row_of inverts the layout on local rows and marks the others -1
+    ro = lay["row_of"]
+    flat = ids.reshape(-1)
+    loc_mask = (flat >= eb) & (flat < eb + nloc)
+    assert np.all(ro[~loc_mask] == -1)
+    assert np.array_equal(s[ro[loc_mask]], np.nonzero(loc_mask)[0])
 
 
 def test_sort_assignment_count_invariant():
