@@ -73,16 +73,37 @@ typedef struct {
  * multiple of block_m; experts without rows get no tile.  Tile i holds rows
  * [i*block_m, (i+1)*block_m) of sorted_token_ids and belongs to expert expert_ids[i].
  * row_of is the inverse: the position of routed row v in sorted_token_ids, or -1 when v's
- * expert is not local. */
+ * expert is not local.
+ * sync is optional scratch of moe_sync_words(T, cap_tiles) int32 words, 16-byte aligned:
+ * moe_sort sets it to zero; moe_fused, when it is given and T < MOE_SINGLE_LAUNCH_MAX_TOKENS,
+ * runs Stage1, Stage2 and the combine as ONE launch whose workgroups count finished work items
+ * in these words (and sets them back to zero before it ends, so the layout can be reused
+ * without sorting again).  Calls that use the same sync words must not overlap in time.
+ * Word 0 is a sticky error flag: nonzero after a wait for another workgroup timed out (about
+ * 0.25 s; the outputs of that call * are then invalid); only moe_sort clears it.  sync == NULL selects one launch per stage, which
+ * measured faster on MI355X at every batch size tried (the single grid must hold Stage1's
+ * register footprint, which lowers Stage2's occupancy); the single launch halves the number of
+ * kernel launches per call, for callers bound by launch overhead. */
 typedef struct {
   int32_t *sorted_token_ids; /* [cap_tiles*block_m] v, or T*topk on padding and unused tiles */
   float *sorted_weights;     /* [cap_tiles*block_m] topk_w[v], 0 on padding; may be NULL */
   int32_t *expert_ids;       /* [cap_tiles] local expert of each tile, -1 past num_tiles */
   int32_t *num_tiles;        /* [1] number of used tiles; written on the device only */
   int32_t *row_of;           /* [T*topk] position of each routed row, -1 if not local */
+  int32_t *sync;             /* [moe_sync_words(T, cap_tiles)] or NULL, see above */
   int32_t cap_tiles;         /* tiles the buffers hold, >= moe_cap_tiles(...) */
   int32_t block_m;           /* rows per tile: 16 or 32 */
 } moe_layout_t;
+
+/* Largest batch (exclusive) that moe_fused runs as one launch when layout->sync is given. */
+#define MOE_SINGLE_LAUNCH_MAX_TOKENS 2048
+/* Column classes per token of the single-launch combine counters. */
+#define MOE_SYNC_CLASSES 16
+
+/* One 64-byte line per counter: a header line, two per tile, MOE_SYNC_CLASSES per token. */
+static inline size_t moe_sync_words(int32_t tokens, int32_t cap_tiles) {
+  return 16 * (1 + 2 * (size_t)cap_tiles + (size_t)MOE_SYNC_CLASSES * (size_t)tokens);
+}
 
 /* Tiles needed in the worst case: sum_e ceil(c_e/bm) <= ceil(T*topk/bm) + min(E, T*topk). */
 static inline int32_t moe_cap_tiles(int32_t tokens, int32_t topk, int32_t num_local_experts,
@@ -143,7 +164,7 @@ static inline size_t moe_fused_ws_bytes(int32_t tokens, int32_t model_dim, int32
  *             layout->sorted_weights is non-NULL.
  *   layout    buffers to fill; cap_tiles >= moe_cap_tiles(tokens, topk, num_local_experts,
  *             block_m), block_m in {16, 32}.  Every entry of all buffers is written (row_of may
- *             be NULL here; moe_fused needs it).
+ *             be NULL here; moe_fused needs it; sync, when given, is set to zero).
  *   ws        device scratch of ws_bytes >= moe_sort_ws_bytes(tokens, topk, num_local_experts).
  * The result is unique and bit-exact: it does not depend on launch order or timing.
  * Limits: 1 <= tokens*topk < 2^31, 1 <= num_local_experts <= 8192. */
@@ -175,16 +196,18 @@ moe_status_t moe_quant_act(const uint16_t *x_bf16, int64_t rows, int64_t cols, i
  *   act       activation and betas (no defaults).
  *   out_bf16  [tokens, D] bf16, overwritten; tokens with no local expert get zeros.
  *   ws        scratch of ws_bytes >= moe_fused_ws_bytes(...).
- *   stages    MOE_STAGE_ALL (both), MOE_STAGE_1 (Stage1 only: clears the accumulator and
- *             leaves the intermediate in ws; `out` untouched) or MOE_STAGE_2 (Stage2 + bf16
- *             finalize only, reading the intermediate a MOE_STAGE_1 call with the same layout
- *             and shapes left in the same ws).  Any other value -> MOE_ERR_INVALID_ARG.
+ *   stages    MOE_STAGE_ALL (both), MOE_STAGE_1 (Stage1 only: leaves the intermediate in
+ *             ws; `out` untouched) or MOE_STAGE_2 (Stage2 + combine only, reading the
+ *             intermediate a MOE_STAGE_1 call with the same layout and shapes left in the same
+ *             ws).  Any other value -> MOE_ERR_INVALID_ARG.  The split calls always use one
+ *             launch per stage.
  * Shapes: D % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED: every K step is one
  * 128-deep block-scaled MFMA); E >= 1.  Stage1 uses fp32 accumulation; the intermediate is
  * stored as bf16 (BF16) or re-encoded with the moe_quant_act rule (FP8, FP4); Stage2
  * accumulates in fp32, stores each routed row's weighted output (fp32 for BF16, bf16
- * otherwise), and a gather kernel sums each token's rows in ascending k in fp32 and rounds to
- * bf16: the result is deterministic.  layout->row_of must be set. */
+ * otherwise), and the combine sums each token's rows in ascending k in fp32 and rounds to
+ * bf16: the result is deterministic, and the single-launch and per-stage paths give the same
+ * bits.  layout->row_of must be set. */
 moe_status_t moe_fused(const void *x, const uint8_t *x_scale, int32_t a_dtype,
                        const uint8_t *w1, const uint8_t *w1_scale,
                        const uint8_t *w2, const uint8_t *w2_scale,

@@ -36,7 +36,8 @@ class MoeError(RuntimeError):
 class Layout(ctypes.Structure):
     _fields_ = [("sorted_token_ids", ctypes.c_void_p), ("sorted_weights", ctypes.c_void_p),
                 ("expert_ids", ctypes.c_void_p), ("num_tiles", ctypes.c_void_p),
-                ("row_of", ctypes.c_void_p), ("cap_tiles", ctypes.c_int32), ("block_m", ctypes.c_int32)]
+                ("row_of", ctypes.c_void_p), ("sync", ctypes.c_void_p), ("cap_tiles", ctypes.c_int32),
+                ("block_m", ctypes.c_int32)]
 
 
 class ActParams(ctypes.Structure):
@@ -92,6 +93,14 @@ def cap_tiles(tokens, topk, num_local_experts, block_m):
     return (n + block_m - 1) // block_m + min(num_local_experts, n)
 
 
+SINGLE_LAUNCH_MAX_TOKENS = 2048
+SYNC_CLASSES = 16
+
+
+def sync_words(tokens, cap):
+    return 16 * (1 + 2 * cap + SYNC_CLASSES * tokens)
+
+
 def sort_ws_bytes(tokens, topk, num_local_experts):
     n = tokens * topk
     chunks = (n + SORT_CHUNK - 1) // SORT_CHUNK
@@ -127,7 +136,9 @@ class MoeLayout:
     """Device buffers of a sorted layout (owned by torch) plus its ctypes view."""
 
     def __init__(self, tokens, topk, num_local_experts, block_m, with_weights=True, device="cuda",
-                 cap=None):
+                 cap=None, single_launch=False):
+        """single_launch: allocate the sync words that let moe_fused run batches below
+        SINGLE_LAUNCH_MAX_TOKENS as one launch (False: one launch per stage)."""
         self.block_m = block_m
         self.cap = cap_tiles(tokens, topk, num_local_experts, block_m) if cap is None else cap
         n = max(self.cap * block_m, 1)
@@ -136,18 +147,21 @@ class MoeLayout:
         self.expert_ids = torch.empty(max(self.cap, 1), dtype=torch.int32, device=device)
         self.num_tiles = torch.empty(1, dtype=torch.int32, device=device)
         self.row_of = torch.empty(max(tokens * topk, 1), dtype=torch.int32, device=device)
+        self.sync = (torch.empty(sync_words(tokens, self.cap), dtype=torch.int32, device=device)
+                     if single_launch else None)
         self.c = Layout(self.sorted_token_ids.data_ptr(),
                         None if self.sorted_weights is None else self.sorted_weights.data_ptr(),
                         self.expert_ids.data_ptr(), self.num_tiles.data_ptr(), self.row_of.data_ptr(),
-                        self.cap, block_m)
+                        None if self.sync is None else self.sync.data_ptr(), self.cap, block_m)
 
 
 def moe_sort(topk_ids, topk_w, expert_begin, num_local_experts, block_m, with_weights=True,
-             layout=None, ws=None):
+             layout=None, ws=None, single_launch=False):
     """Route-sort on the GPU; returns a MoeLayout (see moe_sort in the header)."""
     T, K = topk_ids.shape
     if layout is None:
-        layout = MoeLayout(T, K, num_local_experts, block_m, with_weights, topk_ids.device)
+        layout = MoeLayout(T, K, num_local_experts, block_m, with_weights, topk_ids.device,
+                           single_launch=single_launch)
     if ws is None:
         ws = torch.empty(max(sort_ws_bytes(T, K, num_local_experts), 1), dtype=torch.uint8,
                          device=topk_ids.device)

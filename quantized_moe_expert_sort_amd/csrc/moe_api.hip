@@ -46,7 +46,9 @@ moe_status_t moe_sort(const int32_t* topk_ids, const float* topk_w, int32_t toke
     if (ws_bytes < moe_sort_ws_bytes(tokens, topk, num_local_experts)) return MOE_ERR_WORKSPACE;
   }
   moe::SortLayout L{layout->sorted_token_ids, layout->sorted_weights, layout->expert_ids,
-                    layout->num_tiles, layout->row_of, layout->cap_tiles};
+                    layout->num_tiles, layout->row_of, layout->sync,
+                    layout->sync ? (int64_t)moe_sync_words(tokens, layout->cap_tiles) : 0,
+                    layout->cap_tiles};
   return hip_status(moe::launch_sort(topk_ids, topk_w, n, expert_begin, num_local_experts,
                                      layout->block_m, L, ws, (hipStream_t)stream));
 }
@@ -117,6 +119,7 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   a.inter = base + off_inter;
   a.inter_s = a_dtype == MOE_DT_BF16 ? nullptr : base + off_iscale;
   a.dbg = act->act == MOE_ACT_NONE_TEST ? (float*)(base + off_dbg) : nullptr;
+  a.sync = layout->sync;
   a.out = out_bf16;
   a.T = tokens;
   a.topk = topk;
@@ -130,6 +133,9 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   a.beta = act->beta;
   a.linear_beta = act->linear_beta;
   a.stages = stages;
+  if (layout->sync && tokens < MOE_SINGLE_LAUNCH_MAX_TOKENS && stages == MOE_STAGE_ALL &&
+      act->act != MOE_ACT_NONE_TEST)
+    return hip_status(moe::launch_single(a, (hipStream_t)stream));
   return hip_status(moe::launch_fused(a, (hipStream_t)stream));
 }
 

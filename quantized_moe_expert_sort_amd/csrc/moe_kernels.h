@@ -14,6 +14,8 @@ struct SortLayout {
   int32_t* expert_ids;
   int32_t* num_tiles;
   int32_t* row_of;        // may be null
+  int32_t* sync;          // may be null; zeroed when given
+  int64_t sync_words;
   int64_t cap_tiles;
 };
 
@@ -43,6 +45,7 @@ struct FusedArgs {
   int2* groups;            // [cap] tile groups (large-batch path)
   int32_t* num_groups;     // [1]
   float* dbg;              // [cap*bm, 2I] raw gate/up sums (NONE_TEST) or null
+  int32_t* sync;           // completion counters of the single-launch path or null
   uint16_t* out;           // [T, D] bf16
   int T, topk, E, D, I, cap_tiles, block_m, a_dtype, act;
   float beta, linear_beta;
@@ -55,5 +58,23 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
 bool tiled_path_supported(const FusedArgs& a);
 hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipStream_t s);
 constexpr int TILED_MIN_TOKENS = 2048;
+
+// Single-launch path (moe_single.hip): Stage1, Stage2 and the combine in one grid whose
+// workgroups signal each other through the layout's sync words.
+hipError_t launch_single(const FusedArgs& a, hipStream_t s);
+
+// Word offsets inside the sync array.  Every counter has a 64-byte line of its own: device-scope
+// atomics on one line are serialized (about 11 ns each on gfx950), whatever word they touch.
+//   line 0               word 0: sticky timeout flag
+//   lines 1 .. cap       Stage1 items finished, per tile
+//   next cap lines       Stage2 items finished, per tile
+//   next 16*T lines      (row, column block) pairs finished, per (token, column class)
+constexpr int64_t SYNC_LINE = 16;
+constexpr int64_t SYNC_ERR = 0;
+__host__ __device__ inline int64_t sync_done1(int64_t cap, int64_t tile) { (void)cap; return SYNC_LINE * (1 + tile); }
+__host__ __device__ inline int64_t sync_done2(int64_t cap, int64_t tile) { return SYNC_LINE * (1 + cap + tile); }
+__host__ __device__ inline int64_t sync_token(int64_t cap, int64_t t, int cls) {
+  return SYNC_LINE * (1 + 2 * cap + (int64_t)MOE_SYNC_CLASSES * t + cls);
+}
 
 }  // namespace moe

@@ -12,6 +12,8 @@
 //   rows <= CHUNK : one workgroup does counting, scan, padding and scatter.
 //   larger        : count (one workgroup per chunk) -> scan (one workgroup)
 //                   -> scatter (one workgroup per chunk).
+// The layout's optional sync words are zeroed by the single-wave / single-workgroup kernel or,
+// on the multi-chunk path, by the counting kernel.
 #include "moe_kernels.h"
 #include "moe_device.h"
 
@@ -161,6 +163,13 @@ __device__ void layout_from_counts(int* counts, int E, int block_m, int sentinel
   if (threadIdx.x == 0) *L.num_tiles = total;
 }
 
+// The layout's sync words (a multiple of 4, 16-byte aligned) set to zero by threads
+// first, first + stride, ...
+__device__ __forceinline__ void zero_sync(const SortLayout& L, int64_t first, int64_t stride) {
+  uint4* p = reinterpret_cast<uint4*>(L.sync);
+  for (int64_t i = first; i < L.sync_words / 4; i += stride) p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
 // ---------------------------------------------------------------- one-wave path (rows <= 64)
 //
 // Lane i holds row v = i.  Its rank is the number of lower lanes with the same expert; the
@@ -211,6 +220,7 @@ __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restri
     L.sorted_ids[p] = sentinel;
     if (L.sorted_w) L.sorted_w[p] = 0.0f;
   }
+  zero_sync(L, lane, WAVE);
   if (lane == 0) *L.num_tiles = total;
 }
 
@@ -225,6 +235,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
   uint16_t* wc = reinterpret_cast<uint16_t*>(tmp + SORT_WAVES + 1);   // [SORT_WAVES][E]
   int key[ROUNDS], rank[ROUNDS];
   rank_chunk(ids, 0, n, expert_begin, E, wc, pos, key, rank);
+  zero_sync(L, threadIdx.x, SORT_THREADS);
   layout_from_counts<SORT_THREADS>(pos, E, block_m, n, L, tmp);
   __syncthreads();
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
 
 __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
     const int32_t* __restrict__ ids, int64_t n, int expert_begin, int E, int* __restrict__ hist,
-    int* __restrict__ ranks) {
+    int* __restrict__ ranks, SortLayout L) {
   extern __shared__ int smem[];
   int* tot = smem;                                             // [E]
   uint16_t* wc = reinterpret_cast<uint16_t*>(tot + E);         // [SORT_WAVES][E]
@@ -254,6 +265,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
   const int n_in = (int)(n - base < MOE_SORT_CHUNK ? n - base : MOE_SORT_CHUNK);
   int key[ROUNDS], rank[ROUNDS];
   rank_chunk(ids, base, n_in, expert_begin, E, wc, tot, key, rank);
+  zero_sync(L, (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x, (int64_t)gridDim.x * SORT_THREADS);
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r)
@@ -325,7 +337,7 @@ hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, 
   int* hist = (int*)ws;
   int* ranks = (int*)((char*)ws + moe_align256((size_t)nchunks * E * sizeof(int)));
   sort_count_kernel<<<nchunks, SORT_THREADS, (size_t)E * sizeof(int) + wc_bytes, s>>>(
-      topk_ids, n, expert_begin, E, hist, ranks);
+      topk_ids, n, expert_begin, E, hist, ranks, L);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scan_kernel<<<1, SCAN_THREADS, (size_t)(E + SCAN_THREADS / WAVE + 1) * sizeof(int), s>>>(

@@ -41,8 +41,20 @@ def test_header_size_helpers_match_binding():
     assert qm.cap_tiles(0, 16, 896, 16) == 0
 
 
-def _layout(cap=100, bm=16, weights=True, row_of=True):
-    return qm.Layout(P.value, P.value if weights else None, P.value, P.value, P.value if row_of else None, cap, bm)
+def test_layout_struct_matches_header():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^{}]*)\} moe_layout_t;", src).group(1)
+    fields = re.findall(r"(\w+)\s*\*?\s*(\w+)\s*;", body)
+    names = [n for _, n in fields]
+    assert names == [f[0] for f in qm.Layout._fields_]
+    for (ctype, name), (_, pytype) in zip(fields, qm.Layout._fields_):
+        is_ptr = re.search(r"\*\s*" + name + r"\s*;", body) is not None
+        assert (pytype is ctypes.c_void_p) == is_ptr, name
+
+
+def _layout(cap=100, bm=16, weights=True, row_of=True, sync=True):
+    return qm.Layout(P.value, P.value if weights else None, P.value, P.value, P.value if row_of else None,
+                     P.value if sync else None, cap, bm)
 
 
 def _sort(ids=P, w=P, T=4, K=2, eb=0, E=8, layout=None, ws=P, ws_bytes=1 << 20):
@@ -60,7 +72,7 @@ def test_sort_validation():
     assert _sort(layout=_layout(bm=64)) == UNSUPPORTED
     assert _sort(layout=_layout(cap=qm.cap_tiles(4, 2, 8, 16) - 1)) == CAPACITY
     assert _sort(w=None) == INVALID                     # sorted_weights requested, no topk_w
-    lay = qm.Layout(None, None, P.value, P.value, P.value, 100, 16)
+    lay = qm.Layout(None, None, P.value, P.value, P.value, None, 100, 16)
     assert _sort(layout=lay) == INVALID
     big = 2000
     assert _sort(T=big, K=16, E=8, layout=_layout(cap=qm.cap_tiles(big, 16, 8, 16)), ws_bytes=16) == WORKSPACE
