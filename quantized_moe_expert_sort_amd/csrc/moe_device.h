@@ -78,17 +78,48 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
 }
 
-__device__ __forceinline__ float fast_tanh(float x) { return 2.0f * fast_sigmoid(2.0f * x) - 1.0f; }
-
 // SiTUv2 (github ROCm/aiter PR 6259, "Motivation"):
 //   y = beta*tanh(g/beta)*sigmoid(g) * lb*tanh(u/lb); inv_* are 1/beta and 1/lb.
+// Evaluated with tanh(x) = sign(x) * (2*sigmoid(2|x|) - 1) = sign(x) * (1 - a) / (1 + a),
+// a = e^(-2|x|), and sigmoid(g) = (g < 0 ? b : 1) / (1 + b), b = e^(-|g|): three exponentials
+// of non-positive arguments (no overflow) and one reciprocal of a product in [1, 8].
 __device__ __forceinline__ float situv2(float g, float u, float beta, float inv_beta, float lb,
                                         float inv_lb) {
-  return beta * fast_tanh(g * inv_beta) * fast_sigmoid(g) * (lb * fast_tanh(u * inv_lb));
+  constexpr float LOG2E = 1.4426950408889634f;
+  const float ag = __builtin_fabsf(g), au = __builtin_fabsf(u);
+  const float a = __builtin_amdgcn_exp2f(ag * (-2.0f * LOG2E * inv_beta));
+  const float b = __builtin_amdgcn_exp2f(ag * -LOG2E);
+  const float c = __builtin_amdgcn_exp2f(au * (-2.0f * LOG2E * inv_lb));
+  const float num = (1.0f - a) * (1.0f - c) * (g < 0.0f ? b : 1.0f);
+  const float den = (1.0f + a) * (1.0f + b) * (1.0f + c);
+  const float y = (beta * lb) * num * __builtin_amdgcn_rcpf(den);
+  return __uint_as_float(__float_as_uint(y) ^ ((__float_as_uint(g) ^ __float_as_uint(u)) & 0x80000000u));
 }
 
 // SiLU epilogue (github ROCm/aiter PR 4471, "Motivation"): silu(g) * u.
 __device__ __forceinline__ float silu_mul(float g, float u) { return g * fast_sigmoid(g) * u; }
+
+// ------------------------------------------------------------------ lane exchanges (DPP)
+//
+// Inside each row of 16 lanes, without an LDS round trip: the value of lane l ^ 1, and the
+// maximum over the row (quad butterflies, then rotations by 4 and 8 lanes).
+
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+}
+
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  uint32_t o;
+  o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);      // quad_perm [1,0,3,2]
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);      // quad_perm [2,3,0,1]
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);     // row_ror:4
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);     // row_ror:8
+  v = o > v ? o : v;
+  return v;
+}
 
 // ------------------------------------------------------------------ 1x32 block encoder
 //
@@ -107,29 +138,37 @@ __device__ __forceinline__ int block_sexp(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Magnitude code of |v| (bit pattern abits, finite) divided by 2^sexp.
+// Magnitude code of |v| (bit pattern abits, finite) divided by 2^sexp.  Branch-free: every
+// case is computed and the result selected, so a wave never splits on the data.
 template <class F>
 __device__ __forceinline__ uint32_t encode_mag(uint32_t abits, int sexp) {
-  if (abits == 0) return 0;
-  uint32_t m;
-  int e;                                   // |v| = m * 2^e, m < 2^24
-  if (abits >= 0x00800000u) { m = (abits & 0x7FFFFFu) | 0x800000u; e = (int)(abits >> 23) - 150; }
-  else { m = abits; e = -149; }
-  const int L = (31 - __clz(m)) + e - sexp;            // floor(log2(|v| / 2^sexp))
+  const bool normal = abits >= 0x00800000u;
+  const uint32_t m = normal ? ((abits & 0x7FFFFFu) | 0x800000u) : abits;   // |v| = m * 2^e, m < 2^24
+  const int e = normal ? (int)(abits >> 23) - 150 : -149;
+  const int L = (31 - (int)__clz(m)) + e - sexp;       // floor(log2(|v| / 2^sexp)) (m > 0)
   const int Lc = L > F::EMIN ? L : F::EMIN;            // subnormals share the lowest binade
   const int shift = (Lc - F::MBITS) - (e - sexp);      // quanta of size 2^(Lc - MBITS)
-  uint32_t n;
-  if (shift <= 0) {
-    n = m << (-shift);
-  } else if (shift > 31) {
-    n = 0;
-  } else {
-    n = m >> shift;
-    const uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
-    n += (rem > half || (rem == half && (n & 1u))) ? 1u : 0u;
-  }
+  const int sh = shift < 1 ? 1 : (shift > 31 ? 31 : shift);
+  uint32_t n = m >> sh;
+  const uint32_t rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  n += (rem > half || (rem == half && (n & 1u))) ? 1u : 0u;     // nearest, ties to even
+  n = shift > 31 ? 0u : n;
+  n = shift <= 0 ? (m << ((-shift) & 31)) : n;         // exact (not reached by e4m3 / e2m1)
   const uint32_t code = ((uint32_t)(Lc - F::EMIN + 1) << F::MBITS) + n - (1u << F::MBITS);
-  return code < (uint32_t)F::MAXCODE ? code : (uint32_t)F::MAXCODE;
+  const uint32_t r = code < (uint32_t)F::MAXCODE ? code : (uint32_t)F::MAXCODE;
+  return abits == 0u ? 0u : r;
+}
+
+// Element code and block scale byte of one element of a block whose largest magnitude has the
+// bit pattern amax: Inf / NaN in the block -> scale 255 and code 0; an all-zero block -> scale
+// 0 and the element's sign; else the rule above.  Branch-free.
+template <class F>
+__device__ __forceinline__ uint32_t encode_in_block(uint32_t bits, uint32_t amax, uint32_t* scale_byte) {
+  const int sexp = block_sexp<F>(amax > 0u && amax < 0x7F800000u ? amax : 0x3F800000u);
+  const uint32_t sign = (bits >> 31) ? (uint32_t)F::SIGN : 0u;
+  const uint32_t c = encode_mag<F>(bits & 0x7FFFFFFFu, sexp) | sign;
+  *scale_byte = amax >= 0x7F800000u ? 255u : (amax == 0u ? 0u : (uint32_t)(sexp + 127));
+  return amax >= 0x7F800000u ? 0u : c;
 }
 
 // Reduce |v| bit patterns over the 32 lanes of a half-wave (xor shuffles stay inside it).
@@ -147,14 +186,8 @@ __device__ __forceinline__ uint32_t halfwave_max_u32(uint32_t v) {
 template <class F>
 __device__ __forceinline__ uint32_t block_encode_lane(float v, uint32_t* scale_byte) {
   const uint32_t bits = __float_as_uint(v);
-  const uint32_t abits = bits & 0x7FFFFFFFu;
-  const uint32_t amax = halfwave_max_u32(abits);
-  const uint32_t sign = (bits >> 31) ? (uint32_t)F::SIGN : 0u;
-  if (amax >= 0x7F800000u) { *scale_byte = 255u; return 0u; }          // Inf / NaN in block
-  if (amax == 0u) { *scale_byte = 0u; return sign; }
-  const int sexp = block_sexp<F>(amax);
-  *scale_byte = (uint32_t)(sexp + 127);
-  return encode_mag<F>(abits, sexp) | sign;
+  const uint32_t amax = halfwave_max_u32(bits & 0x7FFFFFFFu);
+  return encode_in_block<F>(bits, amax, scale_byte);
 }
 
 }  // namespace moe

@@ -1,0 +1,552 @@
+// Large-batch Stage1 / Stage2: LDS-tiled block-scaled grouped GEMMs over groups of sort tiles.
+//
+// With many routed rows per expert (prefill, expert-parallel shards) the per-tile items of
+// moe_stage_items.h re-stream an expert's weights for every 16/32-row tile.  Here a work item
+// is (group, column block): a group is up to GT consecutive sort tiles of one expert (an
+// expert's tiles are split into groups of balanced size), so each weight byte fetched serves
+// up to GT*32 rows, and a column block is BNW weight rows.  Eight waves in a 2 (rows) x 4
+// (weight rows) grid each compute a 128 x 64 sub-tile with v_mfma_scale_f32_16x16x128_f8f6f4
+// (fp8 x fp4 or fp4 x fp4); 16-row fragments past the group's rows are skipped.  Waves w and
+// w + 4 share a SIMD and own the two row halves, so every SIMD does the same work whatever
+// the group's row count.
+//
+// Operand staging: per 128-deep K step the A rows (gathered activations or intermediate rows),
+// the B rows (fp4 weights) and the e8m0 scale dwords of both are copied global -> LDS by the
+// load-to-LDS instructions (global_load_lds_dwordx4 / _dword: lane l of a wave instruction
+// writes bytes [16l, 16l+16) (or [4l, 4l+4)) after the wave's LDS address in m0), P steps in
+// flight (P LDS buffers), one barrier per step.  The copies are issued from inline assembly,
+// so the only waits on them are the explicit vmcnt waits of the pipeline.  The 16-byte chunks
+// of a row are stored XOR-swizzled (chunk p of row r at position p ^ swz(r)), so the 16 lanes
+// that read one chunk column of 16 rows for a matrix-core operand hit distinct LDS banks.
+//
+// The grid is persistent: one workgroup per CU, each looping over work items.  The items are
+// cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so the column
+// blocks of a group and the groups of an expert share that XCD's L2.
+//
+// Stage1 epilogue (github ROCm/aiter PR 6259 "Technical Details": SiTUv2 in the stage1
+// epilogue): a wave's B rows are [32 gate rows | the matching 32 up rows], so g and u of one
+// output sit in the same lane; y = act(g, u) is re-encoded per 32-column block (PR 4463 "Three
+// tuner defects" item 2: fused fp4 stage1 output) with the block maximum reduced over 16 lanes.
+// Stage2 epilogue: the row result times the router weight, stored as bf16 per routed row for the
+// gather combine.
+#include "moe_kernels.h"
+#include "moe_operands.h"
+
+#include <type_traits>
+
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is written by the load-to-LDS copies
+
+namespace moe {
+
+namespace {
+
+constexpr int GT = 8;                         // sort tiles (of 32 rows) per group, at most
+constexpr int GTHREADS = 512;
+constexpr int GWAVES = GTHREADS / WAVE;       // 8
+constexpr int WM = 2, WN = 4;                 // wave grid: rows x weight rows
+constexpr int BMW = GT * 32;                  // rows per group: 256
+constexpr int BNW = 256;                      // weight rows per column block
+constexpr int MFW = BMW / WM / 16;            // 16-row A fragments per wave: 8
+constexpr int NFW = BNW / WN / 16;            // 16-row B fragments per wave: 4
+constexpr int STG_STRIDE = BNW * 2 + 16;      // LDS row stride of the staged Stage2 output tile
+static_assert(WM * WN == GWAVES, "wave grid");
+
+// ---------------------------------------------------------------- tile groups
+//
+// groups[g] = (first tile, tile count).  The tiles of an expert (a maximal run of equal
+// expert_ids; the sort writes them in ascending expert order) are cut into ceil(n / GT) groups
+// of ceil(n / ceil(n / GT)) tiles (the last one shorter).  One workgroup of 1024 threads: the
+// tile -> expert map is staged in LDS (up to GROUP_LDS_TILES tiles, else read from global
+// memory), each thread owns a contiguous chunk of tiles and finds the bounds of a run by binary
+// search (once per expert it meets), and a workgroup scan of the per-chunk group counts places
+// the groups in tile order.
+
+constexpr int GROUP_THREADS = 1024;
+constexpr int GROUP_LDS_TILES = 16384;
+
+__device__ __forceinline__ int group_size(int len) {
+  const int ng = (len + GT - 1) / GT;
+  return (len + ng - 1) / ng;
+}
+
+__global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __restrict__ expert_ids,
+                                                              const int32_t* __restrict__ num_tiles_p,
+                                                              int cap, int2* __restrict__ groups,
+                                                              int32_t* __restrict__ num_groups) {
+  __shared__ int lds_e[GROUP_LDS_TILES];
+  __shared__ int tmp[GROUP_THREADS / WAVE + 1];
+  const int n = min(*num_tiles_p, cap);
+  const bool in_lds = n <= GROUP_LDS_TILES;
+  if (in_lds)
+    for (int i = threadIdx.x; i < n; i += GROUP_THREADS) lds_e[i] = expert_ids[i];
+  __syncthreads();
+  auto E = [&](int i) { return in_lds ? lds_e[i] : expert_ids[i]; };
+  const int per = (n + GROUP_THREADS - 1) / GROUP_THREADS;
+  const int t0 = threadIdx.x * per, t1 = min(n, t0 + per);
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+
+  // run bounds [rs, re) of tile t's expert; cached while consecutive tiles share the expert
+  int cur_e = INT32_MIN, rs = 0, re = 0;
+  auto bounds = [&](int t) {
+    const int e = E(t);
+    if (e == cur_e) return;
+    cur_e = e;
+    int lo = 0, hi = t;                      // first index with E >= e
+    while (lo < hi) { const int m = (lo + hi) >> 1; if (E(m) < e) lo = m + 1; else hi = m; }
+    rs = lo;
+    lo = t + 1; hi = n;                      // first index with E > e
+    while (lo < hi) { const int m = (lo + hi) >> 1; if (E(m) <= e) lo = m + 1; else hi = m; }
+    re = lo;
+  };
+  int starts = 0;
+  for (int t = t0; t < t1; ++t) {
+    bounds(t);
+    starts += ((t - rs) % group_size(re - rs)) == 0;
+  }
+  int scan = starts;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int o = __shfl_up(scan, d, WAVE);
+    if (lane >= d) scan += o;
+  }
+  if (lane == WAVE - 1) tmp[w] = scan;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < GROUP_THREADS / WAVE; ++i) { const int c = tmp[i]; tmp[i] = run; run += c; }
+    tmp[GROUP_THREADS / WAVE] = run;
+  }
+  __syncthreads();
+  int gidx = tmp[w] + scan - starts;
+  cur_e = INT32_MIN;
+  for (int t = t0; t < t1; ++t) {
+    bounds(t);
+    const int gs = group_size(re - rs);
+    if ((t - rs) % gs == 0) groups[gidx++] = int2{t, min(gs, re - t)};
+  }
+  if (threadIdx.x == 0) *num_groups = tmp[GROUP_THREADS / WAVE];
+}
+
+// ---------------------------------------------------------------- load-to-LDS copies
+
+// 16 bytes per lane: global (base + off) -> LDS (lds + 16 * lane).  base and lds are
+// wave-uniform.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// 4 bytes per lane: global (base + off) -> LDS (lds + 4 * lane).
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// Wait until at most n of this wave's vector memory operations are outstanding (they complete
+// in issue order), then meet the other waves.  lgkmcnt(0): this wave's LDS accesses are done,
+// so a buffer may be refilled once every wave has passed.  n >= 63 waits for nothing.
+__device__ __forceinline__ void wait_and_barrier(int n) {
+  switch (n) {
+#define MOE_WB(k) case k: asm volatile("s_waitcnt vmcnt(" #k ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    MOE_WB(1) MOE_WB(2) MOE_WB(3) MOE_WB(4) MOE_WB(5) MOE_WB(6) MOE_WB(7) MOE_WB(8) MOE_WB(9)
+    MOE_WB(10) MOE_WB(11) MOE_WB(12) MOE_WB(13) MOE_WB(14) MOE_WB(15) MOE_WB(16) MOE_WB(17)
+    MOE_WB(18) MOE_WB(19) MOE_WB(20) MOE_WB(21) MOE_WB(22) MOE_WB(23) MOE_WB(24) MOE_WB(25)
+    MOE_WB(26) MOE_WB(27) MOE_WB(28) MOE_WB(29) MOE_WB(30) MOE_WB(31)
+#undef MOE_WB
+    case 63: asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
+}
+
+// Barrier for LDS data only: pending global stores of this wave are not waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Position of 16-byte chunk `part` of row `row` in a row-major LDS tile with CPR chunks per row.
+// A matrix-core operand read has the 16 lanes of a group read chunk `part` of 16 consecutive
+// rows; the XOR makes those 16 chunks fall in distinct banks whether the LDS serves 16 lanes
+// over 64 four-byte banks or 8 lanes over 32 banks per cycle.  The XOR term depends only on
+// row % 16, so the fragments of a wave differ by constant offsets.
+template <int CPR>
+__device__ __forceinline__ int swz_slot(int row, int part) {
+  if constexpr (CPR == 8) return row * 8 + (part ^ (((row >> 1) ^ (row << 2)) & 7));
+  else return row * 4 + (part ^ ((row ^ (row >> 2)) & 3));
+}
+
+// ---------------------------------------------------------------- grouped GEMM
+//
+// Wave roles.  On gfx9 a wave's loads and stores share one in-order completion counter
+// (vmcnt), so a wave that waits for a load also waits for every store it issued before it.
+// Waves 0..3 (the loaders) therefore issue every global load of the kernel (the operand
+// copies, the row ids and router weights of an item) and never store; waves 4..7 (the
+// storers) issue every global store (the item's output tile, staged in LDS) and never wait on
+// vmcnt, so the output of one item drains while the next item's operands stream in.  All
+// eight waves run the MFMAs.
+
+constexpr int NLOAD = 4;                      // loader waves
+
+template <int ADT>
+struct GFmt {
+  static constexpr int KA = ADT == DT_FP8 ? 128 : 64;     // A bytes per row per K step
+  static constexpr int ACPR = KA / 16;                    // 16-byte chunks per A row
+  static constexpr int P = ADT == DT_FP8 ? 3 : 4;         // LDS buffers = K steps in flight + 1
+  static constexpr int A_BYTES = BMW * KA;
+  static constexpr int B_BYTES = BNW * 64;
+  static constexpr int BUF = A_BYTES + B_BYTES + (BMW + BNW) * 4;
+  static constexpr int A_IPL = A_BYTES / 1024 / NLOAD;    // A copy instructions per loader per step
+  static constexpr int B_IPL = B_BYTES / 1024 / NLOAD;
+  static constexpr int ROWS_PER_AI = 1024 / KA;           // A rows covered by one instruction
+  static constexpr int OB = ADT == DT_FP8 ? BNW / 2 : BNW / 4;   // Stage1 output code bytes per row
+  static constexpr int OBS = OB + 16;                     // their LDS row stride
+};
+
+template <int ADT, int STAGE, int ACT>
+__global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, const int2* __restrict__ groups,
+                                                                  const int32_t* __restrict__ num_groups,
+                                                                  int n_nblk) {
+  using F = GFmt<ADT>;
+  constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P;
+  static_assert(F::A_IPL * NLOAD * 1024 == F::A_BYTES && F::B_IPL * NLOAD * 1024 == F::B_BYTES, "copy split");
+  static_assert(BMW == NLOAD * WAVE && BNW == NLOAD * WAVE, "one scale copy of each operand per loader");
+  static_assert(BMW * STG_STRIDE <= P * F::BUF && BMW * (F::OBS + 4) <= P * F::BUF, "staging fits");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[P * F::BUF];
+  __shared__ int lds_v[BMW];
+  __shared__ float lds_w[BMW];
+
+  const int TK = p.T * p.topk, D = p.D, I = p.I;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
+  const bool loader = wave < NLOAD;
+  const int lw = wave & (NLOAD - 1);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = STAGE == 1 ? D : I;
+  const int S = K / 128;
+  const uint32_t lds0 = lds_addr(lds);
+
+  const int n_act = *num_groups * n_nblk;
+  const int per_xcd = (n_act + 7) / 8;
+  const int xcd = blockIdx.x & 7, local0 = blockIdx.x >> 3, stride = gridDim.x >> 3;
+
+  for (int local = local0; local < per_xcd; local += stride) {
+    const int work = xcd * per_xcd + local;
+    if (work >= n_act) break;
+    const int gi = work / n_nblk, nb = work - gi * n_nblk;
+    const int2 grp = groups[gi];
+    const int tile0 = grp.x, rows_used = grp.y * 32;
+    const int e = p.expert_ids[tile0];
+    const int row_base = tile0 * 32;                      // first layout row of the group
+    if (loader) {
+      const int r = threadIdx.x;                          // < BMW
+      const int v = r < rows_used ? p.sorted_ids[row_base + r] : TK;
+      lds_v[r] = v;
+      if (STAGE == 2) lds_w[r] = (unsigned)v < (unsigned)TK ? p.topk_w[v] : 0.f;
+    }
+    lds_barrier();
+
+    // ---- copy sources.  A: stage1 gathered x rows (padding rows read token 0, their results
+    // are never stored), stage2 the group's intermediate rows.  B: stage1 [gate NI | up NI]
+    // rows of column block nb (NI = BNW/2), stage2 BNW output rows.
+    const size_t a_rowbytes = (size_t)K * KA / 128;
+    const uint8_t* a_base = STAGE == 1 ? p.x : p.inter + (size_t)row_base * a_rowbytes;
+    const uint8_t* as_base = STAGE == 1 ? p.xs : p.inter_s + (size_t)row_base * (K / 32);
+    const uint8_t* b_base = STAGE == 1 ? p.w1 + (size_t)e * 2 * I * (D / 2) : p.w2 + (size_t)e * D * (I / 2);
+    const uint8_t* bs_base = STAGE == 1 ? p.w1s + (size_t)e * 2 * I * (D / 32) : p.w2s + (size_t)e * D * (I / 32);
+    auto b_row = [&](int r) -> int {                      // weight row within the expert
+      if (STAGE == 1) {
+        constexpr int NI = BNW / 2;
+        return r < NI ? nb * NI + r : I + nb * NI + (r - NI);
+      }
+      return nb * BNW + r;
+    };
+    auto a_src_index = [&](int row) -> uint32_t {        // source row of A row `row`
+      if (STAGE == 1) {
+        const int v = lds_v[row];
+        return (uint32_t)((unsigned)v < (unsigned)TK ? v / p.topk : 0);
+      }
+      return (uint32_t)(row < rows_used ? row : 0);
+    };
+    // loader lw issues tile instructions j = i * NLOAD + lw (A rows [j * ROWS_PER_AI, ...));
+    // A instructions wholly past the group's rows are not issued
+    uint32_t a_off[F::A_IPL];
+    int n_ai = 0;
+#pragma unroll
+    for (int i = 0; i < F::A_IPL; ++i) {
+      const int j = i * NLOAD + lw;
+      const int q = j * WAVE + lane;
+      const int row = q / ACPR, part = swz_slot<ACPR>(row, q % ACPR) - row * ACPR;   // the XOR is an involution
+      a_off[i] = a_src_index(row) * (uint32_t)a_rowbytes + part * 16;
+      n_ai += j * F::ROWS_PER_AI < rows_used;
+    }
+    uint32_t b_off[F::B_IPL];
+#pragma unroll
+    for (int i = 0; i < F::B_IPL; ++i) {
+      const int j = i * NLOAD + lw;
+      const int q = j * WAVE + lane;
+      const int row = q / 4, part = swz_slot<4>(row, q % 4) - row * 4;
+      b_off[i] = (uint32_t)b_row(row) * (uint32_t)(K / 2) + part * 16;
+    }
+    // scale dwords: loader lw copies those of A rows and of B rows [64 lw, 64 lw + 64)
+    const int sc_row = lw * WAVE + lane;
+    const bool as_on = lw * WAVE < rows_used;
+    const uint32_t as_off = a_src_index(sc_row) * (uint32_t)(K / 32);
+    const uint32_t bs_off = (uint32_t)b_row(sc_row) * (uint32_t)(K / 32);
+    const int per_step = n_ai + F::B_IPL + (as_on ? 1 : 0) + 1;
+
+    // per step the K advance goes into the (scalar) global base; lane offsets stay fixed
+    auto issue = [&](int s, int buf) {
+      const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * F::BUF);
+      const uint8_t* ab = a_base + s * KA;
+      const uint8_t* bb = b_base + s * 64;
+#pragma unroll
+      for (int i = 0; i < F::A_IPL; ++i)
+        if (i < n_ai) dma16(ab, a_off[i], L + (i * NLOAD + lw) * 1024);
+#pragma unroll
+      for (int i = 0; i < F::B_IPL; ++i)
+        dma16(bb, b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
+      if (as_on) dma4(as_base + s * 4, as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
+      dma4(bs_base + s * 4, bs_off, L + F::A_BYTES + F::B_BYTES + BMW * 4 + lw * 256);
+    };
+
+    // the wave's B fragment rows: stage1 gate rows [32wn, 32wn+32) and the same up rows;
+    // stage2 rows [64wn, 64wn+64)
+    auto b_frag_row = [&](int j) -> int {
+      if (STAGE == 1) return j < 2 ? 32 * wn + 16 * j : BNW / 2 + 32 * wn + 16 * (j - 2);
+      return 64 * wn + 16 * j;
+    };
+    const int arow0 = 128 * wm;                           // the wave's first A row
+    // A fragments of this wave that hold group rows: rows_used is a multiple of 32, so 0, 2, 4,
+    // 6 or 8; the MFMA loop is instantiated per count (no per-fragment branches inside it)
+    const int n_af = max(0, min(MFW, (rows_used - arow0) / 16));
+
+    auto run = [&](auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+      v4f acc[NA > 0 ? NA : 1][NFW];
+#pragma unroll
+      for (int f = 0; f < NA; ++f)
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+      auto compute = [&](int buf) {
+        const uint8_t* la = lds + buf * F::BUF;
+        const uint8_t* lb = la + F::A_BYTES;
+        const uint32_t* las = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
+        const uint32_t* lbs = las + BMW;
+        v8i bop[NFW];
+        uint32_t bsc[NFW];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          const int br = b_frag_row(j) + r16;
+          bop[j] = fp4_operand_lo(*reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16));
+          bsc[j] = (lbs[br] >> (8 * g)) & 0xFFu;
+        }
+        // A fragment f+1 is read from LDS while the MFMAs of fragment f run; the scheduling
+        // barrier keeps the compiler from hoisting every fragment read (register pressure)
+        auto load_a = [&](int f, v8i& aop, uint32_t& asc) {
+          const int ar = arow0 + 16 * f + r16;
+          if (ADT == DT_FP8) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, g) * 16);
+            const uint4 hi = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, 4 + g) * 16);
+            aop = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          } else {
+            aop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
+          }
+          asc = (las[ar] >> (8 * g)) & 0xFFu;
+        };
+        v8i a_cur;
+        uint32_t as_cur;
+        load_a(0, a_cur, as_cur);
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+          v8i a_nxt = a_cur;
+          uint32_t as_nxt = as_cur;
+          if (f + 1 < NA) load_a(f + 1, a_nxt, as_nxt);
+#pragma unroll
+          for (int j = 0; j < NFW; ++j) {
+            if (ADT == DT_FP8) acc[f][j] = mfma_fp8_fp4(a_cur, bop[j], acc[f][j], as_cur, bsc[j]);
+            else acc[f][j] = mfma_fp4_fp4(a_cur, bop[j], acc[f][j], as_cur, bsc[j]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          a_cur = a_nxt;
+          as_cur = as_nxt;
+        }
+      };
+
+      // ---- K loop: steps s+1 .. s+P-2 in flight while step s is computed
+      if (loader) {
+#pragma unroll
+        for (int q = 0; q < P - 1; ++q)
+          if (q < S) issue(q, q);
+      }
+      for (int s = 0; s < S; ++s) {
+        // a loader's copies of step s are done once at most (issued after them) remain
+        wait_and_barrier(loader ? per_step * min(S - 1 - s, P - 2) : 63);
+        if (loader && s + P - 1 < S) issue(s + P - 1, (s + P - 1) % P);   // refills the buffer of step s-1
+        if (NA > 0) compute(s % P);
+      }
+      lds_barrier();                                      // the operand buffers become staging
+
+      // ---- epilogues: the item's output tile is staged in LDS by every wave
+      if (STAGE == 1) {
+        uint8_t* st_codes = lds;                          // [BMW][OBS]
+        uint8_t* st_scales = lds + BMW * F::OBS;          // [BMW][4]: one byte per 32-column block
+        const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = arow0 + 16 * f + 4 * g + i;
+            // one 32-column block: gate fragments 0, 1 with up fragments 2, 3
+            float y[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float gs = acc[f][h][i], us = acc[f][2 + h][i];
+              y[h] = ACT == ACT_SITUV2 ? situv2(gs, us, p.beta, inv_beta, p.linear_beta, inv_lb) : silu_mul(gs, us);
+            }
+            const uint32_t amax =
+                row16_max_u32(max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu));
+            uint32_t code[2], sbyte;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              code[h] = ADT == DT_FP8 ? encode_in_block<Fp8Fmt>(__float_as_uint(y[h]), amax, &sbyte)
+                                      : encode_in_block<Fp4Fmt>(__float_as_uint(y[h]), amax, &sbyte);
+            // every lane writes its own column (32 wn + 16 h + r16 of the block); for fp4 both
+            // lanes of a nibble pair write the same byte, and all 16 lanes the same scale byte
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int c = 32 * wn + 16 * h + r16;
+              if (ADT == DT_FP8) {
+                st_codes[row * F::OBS + c] = (uint8_t)code[h];
+              } else {
+                const uint32_t partner = lane_xor1(code[h]);
+                st_codes[row * F::OBS + c / 2] = (uint8_t)((r16 & 1) ? (partner | (code[h] << 4)) : (code[h] | (partner << 4)));
+              }
+            }
+            st_scales[row * 4 + wn] = (uint8_t)sbyte;
+          }
+        }
+        lds_barrier();
+        if (!loader) {
+          const int t = threadIdx.x - NLOAD * WAVE;
+          constexpr int CPRO = F::OB / 16;
+          const size_t irow = ADT == DT_FP8 ? (size_t)I : (size_t)I / 2;   // intermediate row bytes
+          for (int c = t; c < rows_used * CPRO; c += (GWAVES - NLOAD) * WAVE) {
+            const int row = c / CPRO, part = c - row * CPRO;
+            if ((unsigned)lds_v[row] < (unsigned)TK) {
+              const size_t R = (size_t)row_base + row;
+              *reinterpret_cast<uint4*>(p.inter + R * irow + (size_t)nb * F::OB + part * 16) =
+                  *reinterpret_cast<const uint4*>(st_codes + row * F::OBS + part * 16);
+            }
+          }
+          for (int row = t; row < rows_used; row += (GWAVES - NLOAD) * WAVE) {
+            if ((unsigned)lds_v[row] < (unsigned)TK) {
+              const size_t R = (size_t)row_base + row;
+              *reinterpret_cast<uint32_t*>(p.inter_s + R * (I / 32) + (size_t)nb * 4) =
+                  *reinterpret_cast<const uint32_t*>(st_scales + row * 4);
+            }
+          }
+        }
+      } else {
+        // the weighted bf16 tile; each routed row then leaves as 512 contiguous bytes
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = arow0 + 16 * f + 4 * g + i;
+            const float w = lds_w[row];
+            uint16_t* srow = reinterpret_cast<uint16_t*>(lds + row * STG_STRIDE) + 64 * wn + r16;
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) srow[16 * j] = f32_to_bf16_rne(acc[f][j][i] * w);
+          }
+        }
+        lds_barrier();
+        if (!loader) {
+          const int t = threadIdx.x - NLOAD * WAVE;
+          constexpr int CPRO = BNW * 2 / 16;              // 16-byte chunks per output row
+          // BATCH chunks are read from LDS before any of them is stored
+          constexpr int NT = (GWAVES - NLOAD) * WAVE, BATCH = 4;
+          for (int c0 = t; c0 < rows_used * CPRO; c0 += NT * BATCH) {
+            uint4 val[BATCH];
+            bool ok[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+              const int c = c0 + NT * u;
+              const int row = min(c / CPRO, BMW - 1), part = c % CPRO;
+              ok[u] = c < rows_used * CPRO && (unsigned)lds_v[row] < (unsigned)TK;
+              val[u] = *reinterpret_cast<const uint4*>(lds + row * STG_STRIDE + part * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+              const int c = c0 + NT * u;
+              const int row = c / CPRO, part = c % CPRO;
+              if (ok[u])
+                *reinterpret_cast<uint4*>(p.rowout + (((size_t)row_base + row) * D + (size_t)nb * BNW) * 2 + part * 16) = val[u];
+            }
+          }
+        }
+      }
+    };
+    switch (n_af) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 4: run(std::integral_constant<int, 4>{}); break;
+      case 6: run(std::integral_constant<int, 6>{}); break;
+      default: run(std::integral_constant<int, 8>{}); break;
+    }
+    lds_barrier();                                        // lds_v and the staging tile are reused
+  }
+}
+
+int g_num_cus = 0;
+
+int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
+template <int ADT, int STAGE>
+hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const int32_t* ngroups, hipStream_t s) {
+  const int n_nblk = STAGE == 1 ? (2 * a.I) / BNW : a.D / BNW;
+  const unsigned grid = (unsigned)(num_cus() / 8 * 8);    // one workgroup per CU, a multiple of 8
+  if (STAGE == 2)
+    grouped_gemm_kernel<ADT, 2, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+  else if (a.act == ACT_SITUV2)
+    grouped_gemm_kernel<ADT, 1, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+  else
+    grouped_gemm_kernel<ADT, 1, ACT_SILU><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tiled_path_supported(const FusedArgs& a) {
+  return a.a_dtype != DT_BF16 && a.block_m == 32 && a.act != ACT_NONE && (2 * a.I) % BNW == 0 &&
+         a.D % BNW == 0;
+}
+
+hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipStream_t s) {
+  hipError_t err;
+  if (a.stages & 1) {
+    group_kernel<<<1, GROUP_THREADS, 0, s>>>(a.expert_ids, a.num_tiles, a.cap_tiles, groups, ngroups);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = a.a_dtype == DT_FP8 ? launch_grouped_stage<DT_FP8, 1>(a, groups, ngroups, s)
+                              : launch_grouped_stage<DT_FP4, 1>(a, groups, ngroups, s);
+    if (err != hipSuccess) return err;
+  }
+  if (a.stages & 2) {
+    err = a.a_dtype == DT_FP8 ? launch_grouped_stage<DT_FP8, 2>(a, groups, ngroups, s)
+                              : launch_grouped_stage<DT_FP4, 2>(a, groups, ngroups, s);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -42,6 +42,14 @@ __device__ __forceinline__ v8i fp4_operand(const uint4& q) {
   return r;
 }
 
+// The same operand with dwords 4..7 left undefined: an fp4 operand of the block-scaled MFMA
+// reads only dwords 0..3, so the upper registers of the tuple need not hold anything.
+__device__ __forceinline__ v8i fp4_operand_lo(const uint4& q) {
+  typedef int v4i_ __attribute__((ext_vector_type(4)));
+  const v4i_ lo = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+  return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);

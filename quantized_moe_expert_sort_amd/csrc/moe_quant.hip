@@ -27,21 +27,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     }
     uint32_t code[4];
     uint32_t sbyte;
-    if (amax >= 0x7F800000u) {
-      sbyte = 255u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) code[j] = 0u;
-    } else if (amax == 0u) {
-      sbyte = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) code[j] = (b[j] >> 31) ? (uint32_t)F::SIGN : 0u;
-    } else {
-      const int sexp = block_sexp<F>(amax);
-      sbyte = (uint32_t)(sexp + 127);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        code[j] = encode_mag<F>(b[j] & 0x7FFFFFFFu, sexp) | ((b[j] >> 31) ? (uint32_t)F::SIGN : 0u);
-    }
+    for (int j = 0; j < 4; ++j) code[j] = encode_in_block<F>(b[j], amax, &sbyte);
     if (F::SIGN == 0x80) {
       *reinterpret_cast<uint32_t*>(q + i * 4) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
     } else {
