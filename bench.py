@@ -26,7 +26,7 @@ METRIC = "fused MoE µs/call, TFLOP/s and weight GB/s (% roofline) at 1/256/8192
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}   # dense; fp8 x fp4 at the fp8 rate
 PAGES_US = {("bf16", 1): 28.3}      # a16w4 us1+us2 at 1 token, 3584x384, E=896, top-16 (gfx950)
-TIERS = ["dec-4", "dec-16", "mid-256", "ep-8192", "pre-16384"]
+TIERS = ["dec-4", "dec-16", "mid-64", "mid-256", "mid-1024", "ep-8192", "pre-16384"]
 
 
 def log(*a):
@@ -231,6 +231,72 @@ def traffic_record(kernel):
     return rec.get("kernels", {}).get(kernel)
 
 
+COPY_PROBE_BYTES = 1 << 30      # elementwise float32 negation of 1 GiB: reads and writes 1 GiB
+
+
+def traffic_probe(wl, host_w_dev, n_launch=40):
+    """Launches for the counter passes: the copy probe (3 launches, known bytes) and n_launch
+    Stage1-only launches of workload wl over pre-sorted rotating layouts."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    wb = Workbench(wl, 64, host_w_dev)
+    wb.prepare_stages()
+    for i in range(n_launch):
+        wb.stage(i, wb.qm.STAGE_1)
+    torch.cuda.synchronize()
+    log(f"traffic probe: 3 copy launches, {n_launch} stage1 launches of {wl.name}")
+
+
+def traffic_summarize(fetch_dir, write_dir, wl_name):
+    """HBM bytes per Stage1 launch from the two counter passes (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch), each scaled by what the same counter reads for the copy probe of known size.
+    Writes profiles/traffic.json and returns a markdown table."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                n = r["Kernel_Name"]
+                key = "copy" if "neg" in n else ("stage1" if "stage1_kernel" in n else None)
+                if key:
+                    rows.setdefault(key, []).append(float(r["Counter_Value"]))
+        return rows
+
+    out = {}
+    lines = ["| counter | copy probe (KiB/launch) | expected (KiB) | factor | stage1 (KiB/launch) | stage1 scaled (bytes/launch) |",
+             "|---|---|---|---|---|---|"]
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        k = per_kernel(d, counter)
+        copy_kib = float(np.median(k["copy"]))
+        factor = (COPY_PROBE_BYTES / 1024.0) / copy_kib
+        s1_kib = float(np.mean(k["stage1"]))
+        out[counter] = {"copy_kib": copy_kib, "factor": factor, "stage1_kib": s1_kib,
+                        "stage1_bytes": s1_kib * 1024.0 * factor, "stage1_launches": len(k["stage1"])}
+        lines.append(f"| {counter} | {copy_kib:.0f} | {COPY_PROBE_BYTES // 1024} | {factor:.4f} | {s1_kib:.1f} | "
+                     f"{s1_kib * 1024.0 * factor:.0f} |")
+    rec = {"source_hash": kernel_source_hash(),
+           "kernels": {f"stage1:{wl_name}": {
+               "hbm_bytes_per_launch": round(out["FETCH_SIZE"]["stage1_bytes"] + out["WRITE_SIZE"]["stage1_bytes"]),
+               "fetch_bytes_per_launch": round(out["FETCH_SIZE"]["stage1_bytes"]),
+               "write_bytes_per_launch": round(out["WRITE_SIZE"]["stage1_bytes"]),
+               "copy_factor_fetch": round(out["FETCH_SIZE"]["factor"], 5),
+               "copy_factor_write": round(out["WRITE_SIZE"]["factor"], 5)}}}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return "\n".join(lines)
+
+
 def cpu_baseline(wl, weights_host, budget_s=15.0):
     """The oracle (sort layout + fused operator) on the host, on routings 0, 1, ... until the
     time budget is spent (at least one)."""
@@ -264,7 +330,14 @@ def main():
     ap.add_argument("--routings", type=int, default=64)
     ap.add_argument("--no-tiers", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only the launches for the HBM-traffic counter passes (run under rocprofv3 --pmc)")
+    ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the two counter passes into profiles/traffic.json (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_summarize:
+        print(traffic_summarize(*args.traffic_summarize, args.workload))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -287,6 +360,9 @@ def main():
         return weights[key]
 
     host, dev_w = weights_for(wl)
+    if args.traffic_probe:
+        traffic_probe(wl, dev_w)
+        return
     log(f"workload {wl.name}: preparing {args.routings} routings")
     wb = Workbench(wl, args.routings, dev_w)
     log(f"timing {args.steps} steps after {args.warmup} warmup")
