@@ -19,9 +19,10 @@
 // of a row are stored XOR-swizzled (chunk p of row r at position p ^ swz(r)), so the 16 lanes
 // that read one chunk column of 16 rows for a matrix-core operand hit distinct LDS banks.
 //
-// The grid is persistent: one workgroup per CU, each looping over work items.  The items are
-// cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so the column
-// blocks of a group and the groups of an expert share that XCD's L2.
+// The grid is persistent: one workgroup per CU, each looping over work items.  Groups are
+// dealt to the 8 XCDs round robin (workgroup b runs on XCD b % 8) and the column blocks of a
+// group stay on one XCD, so its activation rows are fetched into one L2 and every XCD gets a
+// similar mix of group sizes.
 //
 // Stage1 epilogue (github ROCm/aiter PR 6259 "Technical Details": SiTUv2 in the stage1
 // epilogue): a wave's B rows are [32 gate rows | the matching 32 up rows], so g and u of one
@@ -226,14 +227,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
   const int S = K / 128;
   const uint32_t lds0 = lds_addr(lds);
 
-  const int n_act = *num_groups * n_nblk;
-  const int per_xcd = (n_act + 7) / 8;
-  const int xcd = blockIdx.x & 7, local0 = blockIdx.x >> 3, stride = gridDim.x >> 3;
+  // groups gi = xcd, xcd + 8, ... run on XCD xcd; item (group, column block)
+  const int ng = *num_groups;
+  const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
+  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_nblk;
 
-  for (int local = local0; local < per_xcd; local += stride) {
-    const int work = xcd * per_xcd + local;
-    if (work >= n_act) break;
-    const int gi = work / n_nblk, nb = work - gi * n_nblk;
+  for (int local = local0; local < items_here; local += stride) {
+    const int gl = local / n_nblk, nb = local - gl * n_nblk;
+    const int gi = gl * 8 + xcd;
     const int2 grp = groups[gi];
     const int tile0 = grp.x, rows_used = grp.y * 32;
     const int e = p.expert_ids[tile0];
