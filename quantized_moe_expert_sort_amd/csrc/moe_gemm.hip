@@ -100,6 +100,109 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
   *reinterpret_cast<uint4*>(out + (size_t)t * D + c) = o;
 }
 
+// ---------------------------------------------------------------- Stage2 + combine, small batches
+//
+// For at most SMALL_ROWS routed rows (decode), one kernel does Stage2 and the combine: workgroup
+// nb owns output columns [16 nb, 16 nb + 16) of every token.  Its eight waves take the layout's
+// tiles round robin; for each tile a wave computes the 16 x 16 block (tile rows x the block's
+// columns) with exactly the MFMA sequence of stage2_item (same operands, K steps ascending),
+// scales it by the router weight and rounds it as stage2_item stores it (fp32 for bf16
+// activations, bf16 otherwise) into slot [t*topk + k] of an LDS array.  The token sums then run
+// over k ascending with 0 for non-local rows, as the combine kernel does: the output has the
+// same bits as Stage2 + combine, without the per-row buffer or the extra launch.
+
+// A wave walks its tiles one at a time, which loses to Stage2 + combine once it has several.
+constexpr int SMALL_ROWS = 32;
+constexpr int SMALL_THREADS = 512;
+constexpr int SMALL_WAVES = SMALL_THREADS / WAVE;
+
+template <int ADT, int BM, int PF>
+__global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p) {
+  constexpr int MF = BM / 16;
+  __shared__ float vals[SMALL_ROWS][16];
+  const int nb = blockIdx.x;
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int TK = p.T * p.topk, D = p.D, I = p.I, S = I / 128;
+  for (int i = threadIdx.x; i < TK * 16; i += SMALL_THREADS) (&vals[0][0])[i] = 0.f;
+  __syncthreads();
+
+  const size_t a_row = (size_t)I * row_bytes_num<ADT>() / row_bytes_den<ADT>();
+  const int ntiles = *p.num_tiles;
+  for (int tile = wave; tile < ntiles; tile += SMALL_WAVES) {
+    int vr[MF], vrow[MF][4];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+      vr[f] = p.sorted_ids[tile * BM + 16 * f + r16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vrow[f][i] = p.sorted_ids[tile * BM + 16 * f + 4 * g + i];
+    }
+    const int e = p.expert_ids[tile];
+    if (e < 0 || e >= p.E) continue;
+    const uint8_t* arow[MF];
+    const uint8_t* asrow[MF];
+    bool aval[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+      const size_t R = (size_t)tile * BM + 16 * f + r16;
+      aval[f] = (unsigned)vr[f] < (unsigned)TK;
+      arow[f] = p.inter + R * a_row;
+      asrow[f] = ADT == DT_BF16 ? nullptr : p.inter_s + R * (I / 32);
+    }
+    const size_t wr = (size_t)e * D + nb * 16 + r16;
+    const uint8_t* brow = p.w2 + wr * (I / 2);
+    const uint8_t* bsrow = p.w2s + wr * (I / 32);
+    v4f acc[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += PF) {
+      uint4 bq[PF];
+      ScaleQuads<PF> bsq;
+      AOperand<ADT> A[PF][MF];
+      ScaleQuads<PF> asq[MF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i)
+        if (s0 + i < S) bq[i] = ld16(brow + (s0 + i) * 64 + 16 * g);
+      bsq.load(bsrow, s0, S, g, true);
+#pragma unroll
+      for (int f = 0; f < MF; ++f) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i)
+          if (s0 + i < S) A[i][f].load(arow[f], s0 + i, g, aval[f]);
+        if (ADT != DT_BF16) asq[f].load(asrow[f], s0, S, g, aval[f]);
+      }
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        if (s0 + i < S) {
+          const uint32_t bs = bsq.get(i, r16, g);
+#pragma unroll
+          for (int f = 0; f < MF; ++f) {
+            const uint32_t as = ADT == DT_BF16 ? 0u : asq[f].get(i, r16, g);
+            acc[f] = A[i][f].mma(bq[i], bs, as, acc[f]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = vrow[f][i];
+        if ((unsigned)v < (unsigned)TK) {
+          const float o = acc[f][i] * p.topk_w[v];
+          vals[v][r16] = ADT == DT_BF16 ? o : __uint_as_float((uint32_t)f32_to_bf16_rne(o) << 16);
+        }
+      }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < p.T * 16; idx += SMALL_THREADS) {
+    const int t = idx >> 4, c = idx & 15;
+    float sum = 0.f;
+    for (int k = 0; k < p.topk; ++k) sum += vals[t * p.topk + k][c];
+    p.out[(size_t)t * D + nb * 16 + c] = f32_to_bf16_rne(sum);
+  }
+}
+
 // Stage tiling per activation dtype and block_m.
 template <int ADT, int BM>
 struct Cfg {
@@ -133,6 +236,10 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   if (!(a.stages & 2) || a.act == ACT_NONE) return hipSuccess;
+  if ((int64_t)a.T * a.topk <= SMALL_ROWS && a.D % 16 == 0) {
+    stage2_small_kernel<ADT, BM, C::PF2><<<(unsigned)(a.D / 16), SMALL_THREADS, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (!(ADT != DT_BF16 && a.T >= TILED_MIN_TOKENS && tiled_path_supported(a))) {
     const unsigned grid2 = (unsigned)((int64_t)a.cap_tiles * n2);
     stage2_kernel<ADT, BM, C::NF2, C::PF2, C::MINW2><<<grid2, THREADS, 0, s>>>(a, a.cap_tiles);

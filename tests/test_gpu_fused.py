@@ -56,6 +56,11 @@ SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
     (61, 20, 3, 256, 128, 0, 20, 32, "fp8", "silu", 0.0),
     (50, 32, 4, 256, 256, 8, 8, 16, "fp8", "situv2", 0.0),       # expert-parallel shard
     (50, 32, 4, 256, 256, 8, 8, 32, "bf16", "situv2", 0.0),
+    # at most 32 routed rows (Stage2 and the combine in one kernel), every a_dtype and block_m
+    (2, 64, 16, 512, 256, 0, 64, 16, "fp8", "situv2", 0.0),
+    (2, 64, 16, 512, 256, 0, 64, 32, "fp4", "situv2", 0.0),
+    (4, 40, 8, 256, 384, 0, 40, 32, "bf16", "silu", 0.0),
+    (8, 32, 4, 256, 256, 8, 8, 16, "fp8", "situv2", 0.0),        # expert-parallel shard
     # >= 2048 tokens with fp8/fp4 activations: the tiled large-batch stages
     (2048, 16, 4, 512, 256, 0, 16, 32, "fp8", "situv2", 1.1),
     (2048, 16, 4, 512, 256, 0, 16, 32, "fp4", "situv2", 1.1),

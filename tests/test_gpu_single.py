@@ -51,6 +51,10 @@ CASES = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act)
     (50, 32, 4, 256, 256, 8, 8, 16, "fp8", "situv2"),            # expert-parallel: tokens w/o rows
     (300, 40, 5, 640, 256, 0, 40, 32, "bf16", "situv2"),
     (2047, 64, 8, 256, 128, 0, 64, 32, "fp8", "situv2"),        # largest single-launch batch
+    # at most 32 routed rows: the per-stage path's fused Stage2 + combine kernel
+    (8, 32, 4, 512, 256, 0, 32, 16, "fp8", "situv2"),            # exactly 32 rows
+    (2, 32, 16, 256, 128, 0, 32, 32, "fp4", "silu"),
+    (6, 32, 4, 256, 256, 8, 8, 16, "fp4", "situv2"),            # expert-parallel: tokens w/o rows
 ]
 
 
