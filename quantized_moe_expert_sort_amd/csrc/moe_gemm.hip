@@ -5,7 +5,11 @@
 //
 // Combine kernel: thread = 8 consecutive columns of one token; it sums that token's routed-row
 // outputs (found through the sort's inverse map row_of) in ascending k and rounds to bf16.
+#include <type_traits>
+
 #include "moe_kernels.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is written by the load-to-LDS copies
 #include "moe_stage_items.h"
 
 namespace moe {
@@ -17,12 +21,13 @@ constexpr int NWAVES = ITEM_WAVES;
 
 // ---------------------------------------------------------------- Stage1
 
-template <int ADT, int BM, int NI, int KW, int PF, int MINW, int ACT>
+template <int ADT, int BM, int NI, int KW, int PF, int MINW, int ACT, bool LDSA>
 __global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, int n_nblk) {
   __shared__ float red[KW][BM][2 * NI + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t astage[LDSA ? KW * AStage<PF>::BYTES : 16];
   const int tile = blockIdx.x / n_nblk;
   const int nb = blockIdx.x - tile * n_nblk;
-  stage1_item<ADT, BM, NI, KW, PF, ACT, false>(p, tile, nb, red);
+  stage1_item<ADT, BM, NI, KW, PF, ACT, false, LDSA>(p, tile, nb, red, astage);
 }
 
 // ---------------------------------------------------------------- Stage2
@@ -103,8 +108,11 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
 // ---------------------------------------------------------------- Stage2 + combine, small batches
 //
 // For at most SMALL_ROWS routed rows (decode), one kernel does Stage2 and the combine: workgroup
-// nb owns output columns [16 nb, 16 nb + 16) of every token.  Its eight waves take the layout's
-// tiles round robin; for each tile a wave computes the 16 x 16 block (tile rows x the block's
+// nb owns output columns [16 nb, 16 nb + 16) of every token.  Its sixteen waves take the layout's
+// tiles round robin (a non-empty expert has at least one row per tile, so at most SMALL_ROWS
+// tiles are in use and a wave has at most two; their expert ids are read together, and the
+// tiles past num_tiles carry expert -1, so num_tiles itself is never waited for); for each
+// tile a wave computes the 16 x 16 block (tile rows x the block's
 // columns) with exactly the MFMA sequence of stage2_item (same operands, K steps ascending),
 // scales it by the router weight and rounds it as stage2_item stores it (fp32 for bf16
 // activations, bf16 otherwise) into slot [t*topk + k] of an LDS array.  The token sums then run
@@ -113,8 +121,10 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
 
 // A wave walks its tiles one at a time, which loses to Stage2 + combine once it has several.
 constexpr int SMALL_ROWS = 32;
-constexpr int SMALL_THREADS = 512;
+constexpr int SMALL_THREADS = 1024;
 constexpr int SMALL_WAVES = SMALL_THREADS / WAVE;
+constexpr int SMALL_TPW = SMALL_ROWS / SMALL_WAVES;   // tiles per wave
+static_assert(SMALL_ROWS % SMALL_WAVES == 0, "every tile in use belongs to one wave");
 
 template <int ADT, int BM, int PF>
 __global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p) {
@@ -128,17 +138,40 @@ __global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p
   __syncthreads();
 
   const size_t a_row = (size_t)I * row_bytes_num<ADT>() / row_bytes_den<ADT>();
-  const int ntiles = *p.num_tiles;
-  for (int tile = wave; tile < ntiles; tile += SMALL_WAVES) {
+  // expert ids and row ids of every tile of this wave, requested together
+  int eid[SMALL_TPW], vrq[SMALL_TPW][MF], vrowq[SMALL_TPW][MF][4];
+#pragma unroll
+  for (int q = 0; q < SMALL_TPW; ++q) {   // unconditional loads (a tile past cap reads the last)
+    const int tile = min(wave + SMALL_WAVES * q, p.cap_tiles - 1);
+    eid[q] = p.expert_ids[tile];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+      vrq[q][f] = p.sorted_ids[tile * BM + 16 * f + r16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vrowq[q][f][i] = p.sorted_ids[tile * BM + 16 * f + 4 * g + i];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < SMALL_TPW; ++q)
+    if (wave + SMALL_WAVES * q >= p.cap_tiles) eid[q] = -1;
+#pragma unroll
+  for (int q = 0; q < SMALL_TPW; ++q) {
+    const int tile = wave + SMALL_WAVES * q;
+    const int e = eid[q];
+    if (e < 0 || e >= p.E) continue;
     int vr[MF], vrow[MF][4];
 #pragma unroll
     for (int f = 0; f < MF; ++f) {
-      vr[f] = p.sorted_ids[tile * BM + 16 * f + r16];
+      vr[f] = vrq[q][f];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vrow[f][i] = p.sorted_ids[tile * BM + 16 * f + 4 * g + i];
+      for (int i = 0; i < 4; ++i) vrow[f][i] = vrowq[q][f][i];
     }
-    const int e = p.expert_ids[tile];
-    if (e < 0 || e >= p.E) continue;
+    // router weights of the accumulator rows, requested with the operands
+    float wv[MF][4];
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[f][i] = (unsigned)vrow[f][i] < (unsigned)TK ? p.topk_w[vrow[f][i]] : 0.f;
     const uint8_t* arow[MF];
     const uint8_t* asrow[MF];
     bool aval[MF];
@@ -155,25 +188,30 @@ __global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p
     v4f acc[MF];
 #pragma unroll
     for (int f = 0; f < MF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += PF) {
+    // scales and intermediate rows first, weights last: the MFMAs of step i wait only for the
+    // weights of steps <= i (loads complete in order)
+    auto chunk = [&](int s0, auto full) {
+      constexpr bool FULL = decltype(full)::value;
       uint4 bq[PF];
       ScaleQuads<PF> bsq;
       AOperand<ADT> A[PF][MF];
       ScaleQuads<PF> asq[MF];
-#pragma unroll
-      for (int i = 0; i < PF; ++i)
-        if (s0 + i < S) bq[i] = ld16(brow + (s0 + i) * 64 + 16 * g);
       bsq.load(bsrow, s0, S, g, true);
 #pragma unroll
-      for (int f = 0; f < MF; ++f) {
-#pragma unroll
-        for (int i = 0; i < PF; ++i)
-          if (s0 + i < S) A[i][f].load(arow[f], s0 + i, g, aval[f]);
+      for (int f = 0; f < MF; ++f)
         if (ADT != DT_BF16) asq[f].load(asrow[f], s0, S, g, aval[f]);
-      }
+#pragma unroll
+      for (int i = 0; i < PF; ++i)
+        if (FULL || s0 + i < S)
+#pragma unroll
+          for (int f = 0; f < MF; ++f) A[i][f].load(arow[f], s0 + i, g, aval[f]);
+#pragma unroll
+      for (int i = 0; i < PF; ++i)
+        if (FULL || s0 + i < S) bq[i] = ld16(brow + (s0 + i) * 64 + 16 * g);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
-        if (s0 + i < S) {
+        if (FULL || s0 + i < S) {
           const uint32_t bs = bsq.get(i, r16, g);
 #pragma unroll
           for (int f = 0; f < MF; ++f) {
@@ -182,14 +220,17 @@ __global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p
           }
         }
       }
-    }
+    };
+    int s0 = 0;
+    for (; s0 + PF <= S; s0 += PF) chunk(s0, std::true_type{});
+    if (s0 < S) chunk(s0, std::false_type{});
 #pragma unroll
     for (int f = 0; f < MF; ++f)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = vrow[f][i];
         if ((unsigned)v < (unsigned)TK) {
-          const float o = acc[f][i] * p.topk_w[v];
+          const float o = acc[f][i] * wv[f][i];
           vals[v][r16] = ADT == DT_BF16 ? o : __uint_as_float((uint32_t)f32_to_bf16_rne(o) << 16);
         }
       }
@@ -210,6 +251,7 @@ struct Cfg {
   static constexpr int KW = 4;                                // waves splitting K in stage1
   static constexpr int PF1 = (ADT == DT_BF16 && BM == 16) ? 7 : 4;   // K steps in flight per wave
   static constexpr int MINW1 = 2;                               // waves per SIMD kept
+  static constexpr bool LDSA = ADT == DT_BF16 && BM == 16;      // activation rows staged in LDS
   static constexpr int NF2 = BM == 16 ? 4 : 2;                // stage2 16-column fragments / wave
   static constexpr int PF2 = 3;                               // K steps in flight (I = 384: all)
   static constexpr int MINW2 = 2;
@@ -226,12 +268,22 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
     hipError_t err = launch_tiled(a, a.groups, a.num_groups, s);
     if (err != hipSuccess || !(a.stages & 2)) return err;
   } else if (a.stages & 1) {
-    if (a.act == ACT_SITUV2)
-      stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SITUV2><<<grid1, T1, 0, s>>>(a, n1);
-    else if (a.act == ACT_SILU)
-      stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SILU><<<grid1, T1, 0, s>>>(a, n1);
-    else
-      stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_NONE><<<grid1, T1, 0, s>>>(a, n1);
+    // the staged copies address x with 32-bit offsets
+    if (C::LDSA && (int64_t)a.T * a.D * 2 < ((int64_t)1 << 31)) {
+      if (a.act == ACT_SITUV2)
+        stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SITUV2, C::LDSA><<<grid1, T1, 0, s>>>(a, n1);
+      else if (a.act == ACT_SILU)
+        stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SILU, C::LDSA><<<grid1, T1, 0, s>>>(a, n1);
+      else
+        stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_NONE, C::LDSA><<<grid1, T1, 0, s>>>(a, n1);
+    } else {
+      if (a.act == ACT_SITUV2)
+        stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SITUV2, false><<<grid1, T1, 0, s>>>(a, n1);
+      else if (a.act == ACT_SILU)
+        stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_SILU, false><<<grid1, T1, 0, s>>>(a, n1);
+      else
+        stage1_kernel<ADT, BM, C::NI, C::KW, C::PF1, C::MINW1, ACT_NONE, false><<<grid1, T1, 0, s>>>(a, n1);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -182,8 +182,10 @@ __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restri
                                                          SortLayout L) {
   const int lane = threadIdx.x;
   int k = -1;
-  if (lane < n) {
+  float w = 0.0f;
+  if (lane < n) {   // both loads issued together: one memory latency before the stores
     const int id = ids[lane] - expert_begin;
+    if (L.sorted_w) w = topk_w[lane];
     k = (id >= 0 && id < E) ? id : -1;
   }
   const bool valid = k >= 0;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restri
   const int p = off * block_m + rank;
   if (valid) {
     L.sorted_ids[p] = lane;
-    if (L.sorted_w) L.sorted_w[p] = topk_w[lane];
+    if (L.sorted_w) L.sorted_w[p] = w;
   }
   if (L.row_of && lane < n) L.row_of[lane] = valid ? p : -1;
   if (leader) {

@@ -4,8 +4,9 @@
 //
 // Stage1 item (tile, nb) (github ROCm/aiter PR 6259 "Technical Details": SiTUv2 in the stage1
 //   epilogue): block_m sorted rows x NI intermediate columns.  The gate columns [n0, n0+NI)
-//   and the matching up columns [I+n0, I+n0+NI) are computed together, so a lane holds g and u
-//   of the same output element.  KW waves split the K = model_dim reduction into contiguous
+//   and the matching up columns [I+n0, I+n0+NI) are computed together (NI = 8 puts both in one
+//   16-column matrix-core fragment), and g and u of one output element meet in the LDS
+//   reduction.  KW waves split the K = model_dim reduction into contiguous
 //   ranges of 128-deep steps; each lane streams its weight bytes and its gathered activation row
 //   straight from memory into matrix-core operands (every byte is loaded once per item), issuing
 //   the loads of PF steps before the first MFMA that uses them; the partial sums meet in LDS.
@@ -19,6 +20,9 @@
 // Combine: each token's routed-row outputs summed in ascending k in fp32, rounded to bf16.
 #pragma once
 
+#include <stdint.h>
+#include <type_traits>
+
 #include "moe_kernels.h"
 #include "moe_operands.h"
 
@@ -27,20 +31,55 @@ namespace moe {
 constexpr int ITEM_THREADS = 256;
 constexpr int ITEM_WAVES = ITEM_THREADS / WAVE;
 
+// 16 bytes per lane copied from global (base + off) straight to LDS (lds + 16 * lane); base and
+// lds are wave-uniform.  The copy is counted by vmcnt like any vector load.
+__device__ __forceinline__ void dma16_lds(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// bf16 activations of a 16-row tile with few routed rows (decode): instead of every lane group
+// loading its 16-byte pieces of the gathered rows into registers (28 partial-wave loads per row
+// and K range, 16 registers per step), each wave copies the K range of up to NV routed rows
+// into LDS with whole-wave load-to-LDS copies and reads each step's operand from there just
+// before its MFMAs.  Rows without a routed row (and rows of another group when a tile has more
+// than NV) read a zero block.
+template <int PF>
+struct AStage {
+  static constexpr int NV = 4;                       // rows staged at once
+  static constexpr int SLOT = PF * 256;              // bytes of one row's K range (PF steps)
+  static constexpr int ZERO = NV * SLOT;             // 256-byte zero block
+  static constexpr int BYTES = NV * SLOT + 256;      // per wave; NV * SLOT = PF KB of 1 KB copies
+};
+
+// Stage1 K split: wave w of KW takes the 128-deep steps [k_lo, k_hi) of K = D.
+__device__ __forceinline__ int k_lo_of(int D, int w, int KW) { return w * ((D / 128 + KW - 1) / KW); }
+__device__ __forceinline__ int k_hi_of(int D, int w, int KW) {
+  return min(D / 128, (w + 1) * ((D / 128 + KW - 1) / KW));
+}
+
 // ---------------------------------------------------------------- Stage1
 
 // Both items return false without doing anything for a tile with no expert (past num_tiles:
 // the sort writes expert id -1 there), so they can be launched over all cap_tiles tiles.  The
 // tile's row ids and its expert id are loaded together: one memory latency before the weight
 // addresses are known, instead of a chain of dependent loads.
-template <int ADT, int BM, int NI, int KW, int PF, int ACT, bool COH>
+template <int ADT, int BM, int NI, int KW, int PF, int ACT, bool COH, bool LDSA = false>
 __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb,
-                                            float (*red)[BM][2 * NI + 1]) {
+                                            float (*red)[BM][2 * NI + 1], uint8_t* astage = nullptr) {
+  static_assert(!LDSA || (ADT == DT_BF16 && BM == 16), "LDS staging is for bf16 16-row tiles");
   constexpr int NT = KW * WAVE;
   constexpr int MF = BM / 16;
-  constexpr int NF = NI / 16;
-  constexpr int NB = 2 * NF;
-  static_assert((BM * NI) % NT == 0, "the epilogue loop runs the same trip count on every lane");
+  constexpr int NB = 2 * NI / 16;
+  static_assert(NI % 8 == 0, "gate and up columns fill whole 16-column fragments");
+  static_assert((BM * NI) % NT == 0 || (BM * NI) % WAVE == 0 && BM * NI < NT,
+                "every wave of the epilogue runs the same trip count on all of its lanes");
   static_assert(ADT == DT_BF16 || NI % 32 == 0, "a quantized intermediate needs whole 32-column blocks");
 
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
@@ -65,11 +104,14 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     arow[f] = p.x + (size_t)t * a_row;
     asrow[f] = ADT == DT_BF16 ? nullptr : p.xs + (size_t)t * (D / 32);
   }
+  // Operand column c = 16 j + r16 of fragment j: gate column nb*NI + c for c < NI, else up
+  // column I + nb*NI + c - NI.
   const uint8_t* brow[NB];
   const uint8_t* bsrow[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int n = (j < NF) ? nb * NI + 16 * j + r16 : I + nb * NI + 16 * (j - NF) + r16;
+    const int c = 16 * j + r16;
+    const int n = (c < NI) ? nb * NI + c : I + nb * NI + c - NI;
     const size_t wr = (size_t)e * 2 * I + n;
     brow[j] = p.w1 + wr * (D / 2);
     bsrow[j] = p.w1s + wr * (D / 32);
@@ -81,31 +123,38 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int S = D / 128;
-  const int spw = (S + KW - 1) / KW;
-  const int k_lo = wave * spw, k_hi = min(S, k_lo + spw);
-  for (int s0 = k_lo; s0 < k_hi; s0 += PF) {
+  // A chunk of up to PF steps: the scale words and the activation rows are requested first and
+  // the weights last, step by step.  Loads complete in order, so the MFMAs of step i wait only
+  // for the weights of steps <= i and overlap the arrival of the later steps.  A chunk of PF
+  // whole steps has no per-step condition, so its loads and waits are straight-line code.
+  auto chunk = [&](int s0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const int s_end = FULL ? s0 + PF : k_hi_of(D, wave, KW);
     uint4 bq[PF][NB];
     ScaleQuads<PF> bsq[NB];
     ScaleQuads<PF> asq[MF];
     AOperand<ADT> A[PF][MF];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int j = 0; j < NB; ++j) bsq[j].load(bsrow[j], s0, s_end, g, true);
 #pragma unroll
-      for (int i = 0; i < PF; ++i)
-        if (s0 + i < k_hi) bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
-      bsq[j].load(bsrow[j], s0, k_hi, g, true);
-    }
+    for (int f = 0; f < MF; ++f)
+      if (ADT != DT_BF16) asq[f].load(asrow[f], s0, s_end, g, aval[f]);
 #pragma unroll
-    for (int f = 0; f < MF; ++f) {
+    for (int i = 0; i < PF; ++i)
+      if (FULL || s0 + i < s_end)
 #pragma unroll
-      for (int i = 0; i < PF; ++i)
-        if (s0 + i < k_hi) A[i][f].load(arow[f], s0 + i, g, aval[f]);
-      if (ADT != DT_BF16) asq[f].load(asrow[f], s0, k_hi, g, aval[f]);
-    }
+        for (int f = 0; f < MF; ++f) A[i][f].load(arow[f], s0 + i, g, aval[f]);
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      if (FULL || s0 + i < s_end)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
+    // every load of the chunk is issued before the first wait (the scheduler would otherwise
+    // sink the later steps' loads below the first MFMAs, a second memory round trip)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      if (s0 + i < k_hi) {
+      if (FULL || s0 + i < s_end) {
         uint32_t bs[NB], as[MF];
 #pragma unroll
         for (int j = 0; j < NB; ++j) bs[j] = bsq[j].get(i, r16, g);
@@ -117,6 +166,102 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
           for (int j = 0; j < NB; ++j) acc[f][j] = A[i][f].mma(bq[i][j], bs[j], as[f], acc[f][j]);
       }
     }
+  };
+  // The LDS-staged variant of a chunk (bf16, 16-row tiles).
+  using AS = AStage<PF>;
+  uint8_t* const xs = astage + wave * AS::BYTES;
+  uint32_t mask16 = 0, my_j = 0, tok = 0;
+  int ngroups = 0;
+  if constexpr (LDSA) {
+    reinterpret_cast<uint32_t*>(xs + AS::ZERO)[lane] = 0u;
+    mask16 = (uint32_t)__ballot(aval[0]) & 0xFFFFu;        // lanes 0..15 hold rows 0..15
+    my_j = __popc(mask16 & ((1u << r16) - 1u));
+    tok = aval[0] ? (uint32_t)(vr[0] / p.topk) : 0u;
+    ngroups = (__popc(mask16) + AS::NV - 1) / AS::NV;
+  }
+  // copy the K range [s0, s0 + n_s) of routed rows q*NV .. q*NV + NV - 1 of the tile into LDS
+  auto stage_group = [&](int q, int s0, int n_s) {
+    uint32_t m = mask16;
+    for (int k = 0; k < q * AS::NV; ++k) m &= m - 1u;
+    const int nrows = min(AS::NV, __popc(m));
+    uint32_t tk[AS::NV];
+#pragma unroll
+    for (int k = 0; k < AS::NV; ++k) {
+      const int row = m ? __ffs(m) - 1 : 0;
+      tk[k] = (uint32_t)__builtin_amdgcn_readlane((int)tok, row);
+      m &= m - 1u;
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)xs);
+    const int ncopy = (nrows * AS::SLOT + 1023) / 1024;
+#pragma unroll
+    for (int c = 0; c < AS::NV * AS::SLOT / 1024; ++c) {
+      if (c >= ncopy) break;
+      const int o = c * 1024 + lane * 16;
+      const int k = o / AS::SLOT, rem = o - k * AS::SLOT, i = rem >> 8;
+      uint32_t t = tk[0];
+#pragma unroll
+      for (int kk = 1; kk < AS::NV; ++kk) t = k == kk ? tk[kk] : t;
+      const bool ok = k < nrows && i < n_s;
+      const uint32_t off = ok ? t * (uint32_t)a_row + (uint32_t)(s0 + i) * 256u + (uint32_t)(rem & 255) : 0u;
+      dma16_lds(p.x, off, lds0 + c * 1024);
+    }
+  };
+  auto chunk_lds = [&](int s0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const int s_end = FULL ? s0 + PF : k_hi_of(D, wave, KW);
+    const int n_s = s_end - s0;
+    uint4 bq[PF][NB];
+    ScaleQuads<PF> bsq[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bsq[j].load(bsrow[j], s0, s_end, g, true);
+    stage_group(0, s0, n_s);
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      if (FULL || i < n_s)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    // the copies were issued before the PF*NB weight loads: once at most that many loads are
+    // outstanding, the staged rows are in LDS
+    if (FULL) wait_vm<PF * NB>();
+    else wait_vm<0>();
+    int q = 0;
+    do {   // at least one pass, so every weight load is consumed on every path
+      if (q > 0) {   // every operand read of the previous group is done before its rows are replaced
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_group(q, s0, n_s);
+        wait_vm<0>();
+      }
+      const bool in = ((mask16 >> r16) & 1u) && (int)my_j / AS::NV == q;
+      const uint8_t* abase = xs + (in ? ((int)my_j % AS::NV) * AS::SLOT : AS::ZERO) + 64 * g;
+      const int astep = in ? 256 : 0;
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        if (FULL || i < n_s) {
+          AOperand<DT_BF16> A;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint4 v = *reinterpret_cast<const uint4*>(abase + i * astep + 16 * jj);
+            A.a[jj] = as_bf16x8(v.x, v.y, v.z, v.w);
+          }
+          uint32_t bs[NB];
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bs[j] = bsq[j].get(i, r16, g);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[0][j] = A.mma(bq[i][j], bs[j], 0u, acc[0][j]);
+        }
+      }
+    } while (++q < ngroups);
+  };
+
+  const int k_lo = k_lo_of(D, wave, KW), k_hi = k_hi_of(D, wave, KW);
+  int s0 = k_lo;
+  if constexpr (LDSA) {
+    for (; s0 + PF <= k_hi; s0 += PF) chunk_lds(s0, std::true_type{});
+    if (s0 < k_hi) chunk_lds(s0, std::false_type{});
+  } else {
+    for (; s0 + PF <= k_hi; s0 += PF) chunk(s0, std::true_type{});
+    if (s0 < k_hi) chunk(s0, std::false_type{});
   }
 
 #pragma unroll
@@ -136,7 +281,14 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
 #pragma unroll
     for (int w = 0; w < KW; ++w) { gs += red[w][row][col]; us += red[w][row][NI + col]; }
     const int R = tile * BM + row;
-    const bool valid = (unsigned)p.sorted_ids[R] < (unsigned)TK;
+    // the row's sorted id, read from the lanes that loaded it
+    int rv = __shfl(vr[0], row & 15, WAVE);
+#pragma unroll
+    for (int f = 1; f < MF; ++f) {
+      const int o = __shfl(vr[f], row & 15, WAVE);
+      rv = (row >> 4) == f ? o : rv;
+    }
+    const bool valid = (unsigned)rv < (unsigned)TK;
     const int ocol = nb * NI + col;
     if (ACT == ACT_NONE) {
       if (valid) {
@@ -198,6 +350,15 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
     for (int i = 0; i < 4; ++i) vrow[f][i] = p.sorted_ids[tile * BM + 16 * f + 4 * g + i];
   const int e = p.expert_ids[tile];
   if (e < 0 || e >= p.E) return false;
+  // router weights of the accumulator rows, requested before the operands
+  float wrow[MF][4];
+#pragma unroll
+  for (int f = 0; f < MF; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = vrow[f][i];
+      wrow[f][i] = (unsigned)v < (unsigned)TK ? p.topk_w[v] : 0.f;
+    }
 
   const size_t a_row = (size_t)I * row_bytes_num<ADT>() / row_bytes_den<ADT>();
   const uint8_t* arow[MF];
@@ -269,14 +430,6 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
     }
   }
 
-  float wrow[MF][4];
-#pragma unroll
-  for (int f = 0; f < MF; ++f)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = vrow[f][i];
-      wrow[f][i] = (unsigned)v < (unsigned)TK ? p.topk_w[v] : 0.f;
-    }
   // each routed row's weighted output goes to its own row of rowout; padding rows are not
   // written and never read.  bf16 pairs of neighbouring columns are packed into one store.
 #pragma unroll
