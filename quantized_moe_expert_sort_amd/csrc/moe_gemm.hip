@@ -35,11 +35,13 @@ __global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, in
 // Workgroup (tile, column block nb): blockIdx = nb * cap + tile, so the tiles of one column
 // block run together.
 
-template <int ADT, int BM, int NF, int PF, int MINW>
+template <int ADT, int BM, int NF, int PF, int MINW, bool LDSA>
 __global__ __launch_bounds__(THREADS, MINW) void stage2_kernel(FusedArgs p, int cap) {
+  __shared__ __attribute__((aligned(16))) uint8_t astage[LDSA ? S2Stage<ADT, BM>::BYTES : 16];
   const int tile = blockIdx.x % cap;
   const int nb = blockIdx.x / cap;
-  stage2_item<ADT, BM, NF, PF, false>(p, tile, nb, [] {});
+  auto none = [] {};
+  stage2_item<ADT, BM, NF, PF, false, decltype(none)&, LDSA>(p, tile, nb, none, astage);
 }
 
 // ---------------------------------------------------------------- combine
@@ -131,7 +133,8 @@ __global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p
   constexpr int MF = BM / 16;
   __shared__ float vals[SMALL_ROWS][16];
   const int nb = blockIdx.x;
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);   // wave-uniform
   const int r16 = lane & 15, g = lane >> 4;
   const int TK = p.T * p.topk, D = p.D, I = p.I, S = I / 128;
   for (int i = threadIdx.x; i < TK * 16; i += SMALL_THREADS) (&vals[0][0])[i] = 0.f;
@@ -294,7 +297,12 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
   }
   if (!(ADT != DT_BF16 && a.T >= TILED_MIN_TOKENS && tiled_path_supported(a))) {
     const unsigned grid2 = (unsigned)((int64_t)a.cap_tiles * n2);
-    stage2_kernel<ADT, BM, C::NF2, C::PF2, C::MINW2><<<grid2, THREADS, 0, s>>>(a, a.cap_tiles);
+    // staged intermediate rows: the whole K in one chunk, 32-bit copy offsets
+    const int64_t rb = (int64_t)a.I * row_bytes_num<ADT>() / row_bytes_den<ADT>();
+    if (a.I <= S2_I_MAX && a.I <= 128 * C::PF2 && (int64_t)a.cap_tiles * BM * rb < ((int64_t)1 << 31))
+      stage2_kernel<ADT, BM, C::NF2, C::PF2, C::MINW2, true><<<grid2, THREADS, 0, s>>>(a, a.cap_tiles);
+    else
+      stage2_kernel<ADT, BM, C::NF2, C::PF2, C::MINW2, false><<<grid2, THREADS, 0, s>>>(a, a.cap_tiles);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -82,7 +82,8 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
                 "every wave of the epilogue runs the same trip count on all of its lanes");
   static_assert(ADT == DT_BF16 || NI % 32 == 0, "a quantized intermediate needs whole 32-column blocks");
 
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);   // wave-uniform
   const int r16 = lane & 15, g = lane >> 4;
   const int TK = p.T * p.topk, D = p.D, I = p.I;
 
@@ -331,11 +332,28 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
 // wait() runs after the weight loads of the first PF steps are issued and before the first
 // intermediate row is read (the single-launch kernel waits there for the tile's Stage1).
 
-template <int ADT, int BM, int NF, int PF, bool COH, class Wait>
-__device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb, Wait&& wait) {
+// Stage2 with the tile's intermediate rows staged in LDS (inter_dim up to S2_I_MAX, so the
+// whole K fits one chunk of PF steps): the four waves of an item need the same rows, so they
+// are copied once per workgroup with whole-wave load-to-LDS copies instead of being loaded by
+// every wave.  Rows are S2Stage::pitch bytes apart so the 16 rows of an operand read fall in
+// distinct banks.
+constexpr int S2_I_MAX = 384;
+template <int ADT, int BM>
+struct S2Stage {
+  static constexpr int RB_MAX = S2_I_MAX * row_bytes_num<ADT>() / row_bytes_den<ADT>();
+  __host__ __device__ static constexpr int pitch(int rb) { return ((rb >> 4) | 1) << 4; }
+  static constexpr int COPIES = (BM * pitch(RB_MAX) + 1023) / 1024;
+  static constexpr int BYTES = COPIES * 1024;
+};
+
+template <int ADT, int BM, int NF, int PF, bool COH, class Wait, bool LDSA = false>
+__device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb, Wait&& wait,
+                                            uint8_t* astage = nullptr) {
+  static_assert(!LDSA || !COH, "the staged rows come from a previous launch");
   constexpr int MF = BM / 16;
   constexpr int NO = ITEM_WAVES * NF * 16;
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);   // wave-uniform
   const int r16 = lane & 15, g = lane >> 4;
   const int TK = p.T * p.topk, D = p.D, I = p.I;
 
@@ -390,6 +408,76 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
   // columns start at or past D load, compute and store nothing (a wave-uniform condition)
   const bool wave_on = nb * NO + wave * NF * 16 < D;
   const int S = wave_on ? I / 128 : 0;
+  if constexpr (LDSA) {
+    // scales, then this wave's share of the row copies, then the weights; every wave takes part
+    // in the copies and the barrier (also a wave whose columns are past D).  With the whole K
+    // in PF steps (FULL) the loads are straight-line code, so each MFMA waits for its own step.
+    const int RB = (int)a_row, RBP = S2Stage<ADT, BM>::pitch(RB);
+    const int ncopy = (BM * RBP + 1023) / 1024;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)astage);
+    const int wv = wave;
+    constexpr int CPW = (S2Stage<ADT, BM>::COPIES + ITEM_WAVES - 1) / ITEM_WAVES;
+    // source offsets of this wave's copies; a row's validity comes from the lanes holding its id
+    uint32_t coff[CPW];
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int o = (wv + ITEM_WAVES * u) * 1024 + 16 * lane;
+      const int row = min(o / RBP, BM - 1), col = o - (o / RBP) * RBP;
+      int v = __shfl(vr[0], row & 15, WAVE);
+#pragma unroll
+      for (int f = 1; f < MF; ++f) {
+        const int vf = __shfl(vr[f], row & 15, WAVE);
+        v = (row >> 4) == f ? vf : v;
+      }
+      const bool ok = o / RBP < BM && col < RB && (unsigned)v < (unsigned)TK;
+      coff[u] = ok ? (uint32_t)((tile * BM + row) * RB + col) : 0u;
+    }
+    auto run = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      uint4 bq[PF][NF];
+      ScaleQuads<PF> bsq[NF];
+      ScaleQuads<PF> asq[MF];
+#pragma unroll
+      for (int j = 0; j < NF; ++j) bsq[j].load(bsrow[j], 0, S, g, true);
+#pragma unroll
+      for (int f = 0; f < MF; ++f)
+        if (ADT != DT_BF16) asq[f].load(asrow[f], 0, S, g, aval[f]);
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const int c = wv + ITEM_WAVES * u;
+        if (c < ncopy) dma16_lds(p.inter, coff[u], lds0 + c * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < PF; ++i)
+        if (FULL || i < S)
+#pragma unroll
+          for (int j = 0; j < NF; ++j) bq[i][j] = ld16(brow[j] + i * 64 + 16 * g);
+      __builtin_amdgcn_sched_barrier(0);
+      // the copies were issued before this wave's weight loads; the barrier makes every wave's
+      // copies visible
+      if (FULL) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PF * NF) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        if (FULL || i < S) {
+          uint32_t bs[NF], as[MF];
+          AOperand<ADT> A[MF];
+#pragma unroll
+          for (int f = 0; f < MF; ++f) A[f].load(astage + (16 * f + r16) * RBP, i, g, aval[f]);
+#pragma unroll
+          for (int j = 0; j < NF; ++j) bs[j] = bsq[j].get(i, r16, g);
+#pragma unroll
+          for (int f = 0; f < MF; ++f) as[f] = ADT == DT_BF16 ? 0u : asq[f].get(i, r16, g);
+#pragma unroll
+          for (int f = 0; f < MF; ++f)
+#pragma unroll
+            for (int j = 0; j < NF; ++j) acc[f][j] = A[f].mma(bq[i][j], bs[j], as[f], acc[f][j]);
+        }
+      }
+    };
+    if (S == PF) run(std::true_type{});
+    else run(std::false_type{});
+  } else {
   uint4 bq[PF][NF];
   ScaleQuads<PF> bsq[NF];
   auto load_weights = [&](int s0) {
@@ -428,6 +516,7 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
           for (int j = 0; j < NF; ++j) acc[f][j] = A[i][f].mma(bq[i][j], bs[j], as[f], acc[f][j]);
       }
     }
+  }
   }
 
   // each routed row's weighted output goes to its own row of rowout; padding rows are not
