@@ -24,7 +24,7 @@ constexpr int NWAVES = ITEM_WAVES;
 template <int ADT, int BM, int NI, int KW, int PF, int MINW, int ACT, bool LDSA>
 __global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, int n_nblk) {
   __shared__ float red[KW][BM][2 * NI + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t astage[LDSA ? KW * AStage<PF>::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t astage[LDSA ? KW * AStage<ADT, PF>::BYTES : 16];
   const int tile = blockIdx.x / n_nblk;
   const int nb = blockIdx.x - tile * n_nblk;
   stage1_item<ADT, BM, NI, KW, PF, ACT, false, LDSA>(p, tile, nb, red, astage);
@@ -252,9 +252,10 @@ template <int ADT, int BM>
 struct Cfg {
   static constexpr int NI = ADT == DT_BF16 ? 16 : 32;         // intermediate columns / workgroup
   static constexpr int KW = 4;                                // waves splitting K in stage1
-  static constexpr int PF1 = (ADT == DT_BF16 && BM == 16) ? 7 : 4;   // K steps in flight per wave
+  static constexpr int PF1 = BM == 16 ? 7 : 4;                // K steps in flight per wave
   static constexpr int MINW1 = 2;                               // waves per SIMD kept
-  static constexpr bool LDSA = ADT == DT_BF16 && BM == 16;      // activation rows staged in LDS
+  // activation rows staged in LDS (fp8 measured faster with its rows in registers)
+  static constexpr bool LDSA = BM == 16 && ADT != DT_FP8;
   static constexpr int NF2 = BM == 16 ? 4 : 2;                // stage2 16-column fragments / wave
   static constexpr int PF2 = 3;                               // K steps in flight (I = 384: all)
   static constexpr int MINW2 = 2;
@@ -267,8 +268,12 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
   const unsigned grid1 = (unsigned)((int64_t)a.cap_tiles * n1);
   const int n2 = (a.D + NWAVES * C::NF2 * 16 - 1) / (NWAVES * C::NF2 * 16);
   constexpr int T1 = C::KW * WAVE;
-  if (ADT != DT_BF16 && a.T >= TILED_MIN_TOKENS && tiled_path_supported(a)) {
-    hipError_t err = launch_tiled(a, a.groups, a.num_groups, s);
+  const bool tiled = ADT != DT_BF16 && tiled_path_supported(a);
+  const bool tiled1 = tiled && a.T >= TILED_MIN_TOKENS_S1, tiled2 = tiled && a.T >= TILED_MIN_TOKENS_S2;
+  if (tiled1 || (tiled2 && !(a.stages & 1))) {
+    FusedArgs t = a;
+    t.stages = a.stages & ((tiled1 ? 1 : 0) | (tiled2 ? 2 : 0));
+    hipError_t err = launch_tiled(t, a.groups, a.num_groups, s);
     if (err != hipSuccess || !(a.stages & 2)) return err;
   } else if (a.stages & 1) {
     // the staged copies address x with 32-bit offsets
@@ -295,7 +300,7 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
     stage2_small_kernel<ADT, BM, C::PF2><<<(unsigned)(a.D / 16), SMALL_THREADS, 0, s>>>(a);
     return hipGetLastError();
   }
-  if (!(ADT != DT_BF16 && a.T >= TILED_MIN_TOKENS && tiled_path_supported(a))) {
+  if (!tiled2) {
     const unsigned grid2 = (unsigned)((int64_t)a.cap_tiles * n2);
     // staged intermediate rows: the whole K in one chunk, 32-bit copy offsets
     const int64_t rb = (int64_t)a.I * row_bytes_num<ADT>() / row_bytes_den<ADT>();

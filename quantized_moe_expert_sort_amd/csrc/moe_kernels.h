@@ -54,10 +54,13 @@ struct FusedArgs {
 
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
 
-// Large-batch stages (moe_gemm_tiled.hip): tile groups of one expert, LDS-tiled GEMMs.
+// Large-batch stages (moe_gemm_grouped.hip): tile groups of one expert, LDS-tiled GEMMs.
+// The tile groups are built with Stage1, so Stage2 takes the grouped path only where Stage1 does.
 bool tiled_path_supported(const FusedArgs& a);
 hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipStream_t s);
-constexpr int TILED_MIN_TOKENS = 2048;
+constexpr int TILED_MIN_TOKENS_S1 = 2048;   // Stage1 from this batch size
+constexpr int TILED_MIN_TOKENS_S2 = 2048;   // Stage2 from this batch size
+static_assert(TILED_MIN_TOKENS_S1 <= TILED_MIN_TOKENS_S2, "Stage2 reads Stage1's tile groups");
 
 // Single-launch path (moe_single.hip): Stage1, Stage2 and the combine in one grid whose
 // workgroups signal each other through the layout's sync words.

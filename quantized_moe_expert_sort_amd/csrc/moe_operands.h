@@ -73,6 +73,12 @@ struct AOperand<DT_FP8> {
       a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+  // the step's operand from a row staged in LDS (base = the step's first byte)
+  __device__ __forceinline__ void load_lds(const uint8_t* base, int g) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + 16 * g);
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + 64 + 16 * g);
+    a = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
   __device__ __forceinline__ v4f mma(const uint4& bq, uint32_t bs, uint32_t as, const v4f& c) const {
     return mfma_fp8_fp4(a, fp4_operand(bq), c, as, bs);
   }
@@ -84,6 +90,9 @@ struct AOperand<DT_FP4> {
   template <bool COH = false>
   __device__ __forceinline__ void load(const uint8_t* row, int step, int g, bool valid) {
     a = valid ? fp4_operand(ld16<COH>(row + step * 64 + 16 * g)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  __device__ __forceinline__ void load_lds(const uint8_t* base, int g) {
+    a = fp4_operand(*reinterpret_cast<const uint4*>(base + 16 * g));
   }
   __device__ __forceinline__ v4f mma(const uint4& bq, uint32_t bs, uint32_t as, const v4f& c) const {
     return mfma_fp4_fp4(a, fp4_operand(bq), c, as, bs);
@@ -106,6 +115,13 @@ struct AOperand<DT_BF16> {
       } else {
         a[jj] = as_bf16x8(0, 0, 0, 0);
       }
+    }
+  }
+  __device__ __forceinline__ void load_lds(const uint8_t* base, int g) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint4 q = *reinterpret_cast<const uint4*>(base + 64 * g + 16 * jj);
+      a[jj] = as_bf16x8(q.x, q.y, q.z, q.w);
     }
   }
   __device__ __forceinline__ v4f mma(const uint4& bq, uint32_t bs, uint32_t, const v4f& c) const {

@@ -44,18 +44,20 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// bf16 activations of a 16-row tile with few routed rows (decode): instead of every lane group
-// loading its 16-byte pieces of the gathered rows into registers (28 partial-wave loads per row
-// and K range, 16 registers per step), each wave copies the K range of up to NV routed rows
-// into LDS with whole-wave load-to-LDS copies and reads each step's operand from there just
-// before its MFMAs.  Rows without a routed row (and rows of another group when a tile has more
-// than NV) read a zero block.
-template <int PF>
+// Activations of a 16-row tile with few routed rows (decode and mid batches): instead of every
+// lane group loading its 16-byte pieces of the gathered rows into registers (partial-wave loads:
+// 28 per bf16 row and K range), each wave copies the K range of up to NV routed rows into LDS
+// with whole-wave load-to-LDS copies and reads each step's operand from there just before its
+// MFMAs.  Rows without a routed row (and rows of another group when a tile has more than NV)
+// read a zero block.
+template <int ADT, int PF>
 struct AStage {
-  static constexpr int NV = 4;                       // rows staged at once
-  static constexpr int SLOT = PF * 256;              // bytes of one row's K range (PF steps)
-  static constexpr int ZERO = NV * SLOT;             // 256-byte zero block
-  static constexpr int BYTES = NV * SLOT + 256;      // per wave; NV * SLOT = PF KB of 1 KB copies
+  static constexpr int SB = 128 * row_bytes_num<ADT>() / row_bytes_den<ADT>();   // bytes per step
+  static constexpr int SLOT = PF * SB;               // bytes of one row's K range (PF steps)
+  static constexpr int NV = 7168 / SLOT < 16 ? 7168 / SLOT : 16;   // rows staged at once
+  static constexpr int ZERO = NV * SLOT;             // zero block of one step (SB bytes)
+  static constexpr int BYTES = NV * SLOT + 256;      // per wave
+  static constexpr int COPIES = (NV * SLOT + 1023) / 1024;
 };
 
 // Stage1 K split: wave w of KW takes the 128-deep steps [k_lo, k_hi) of K = D.
@@ -73,7 +75,7 @@ __device__ __forceinline__ int k_hi_of(int D, int w, int KW) {
 template <int ADT, int BM, int NI, int KW, int PF, int ACT, bool COH, bool LDSA = false>
 __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb,
                                             float (*red)[BM][2 * NI + 1], uint8_t* astage = nullptr) {
-  static_assert(!LDSA || (ADT == DT_BF16 && BM == 16), "LDS staging is for bf16 16-row tiles");
+  static_assert(!LDSA || BM == 16, "LDS staging is for 16-row tiles");
   constexpr int NT = KW * WAVE;
   constexpr int MF = BM / 16;
   constexpr int NB = 2 * NI / 16;
@@ -145,11 +147,15 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
       if (FULL || s0 + i < s_end)
 #pragma unroll
         for (int f = 0; f < MF; ++f) A[i][f].load(arow[f], s0 + i, g, aval[f]);
+    // one base address per fragment; the steps are immediate offsets of the loads
+    const uint8_t* bbase[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bbase[j] = brow[j] + s0 * 64 + 16 * g;
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       if (FULL || s0 + i < s_end)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
+        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 64);
     // every load of the chunk is issued before the first wait (the scheduler would otherwise
     // sink the later steps' loads below the first MFMAs, a second memory round trip)
     __builtin_amdgcn_sched_barrier(0);
@@ -168,8 +174,8 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
       }
     }
   };
-  // The LDS-staged variant of a chunk (bf16, 16-row tiles).
-  using AS = AStage<PF>;
+  // The LDS-staged variant of a chunk (16-row tiles).
+  using AS = AStage<ADT, PF>;
   uint8_t* const xs = astage + wave * AS::BYTES;
   uint32_t mask16 = 0, my_j = 0, tok = 0;
   int ngroups = 0;
@@ -185,7 +191,7 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     uint32_t m = mask16;
     for (int k = 0; k < q * AS::NV; ++k) m &= m - 1u;
     const int nrows = min(AS::NV, __popc(m));
-    uint32_t tk[AS::NV];
+    uint32_t tk[AS::NV];                                     // tokens of the group's rows
 #pragma unroll
     for (int k = 0; k < AS::NV; ++k) {
       const int row = m ? __ffs(m) - 1 : 0;
@@ -195,15 +201,17 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)xs);
     const int ncopy = (nrows * AS::SLOT + 1023) / 1024;
 #pragma unroll
-    for (int c = 0; c < AS::NV * AS::SLOT / 1024; ++c) {
+    for (int c = 0; c < AS::COPIES; ++c) {
       if (c >= ncopy) break;
-      const int o = c * 1024 + lane * 16;
-      const int k = o / AS::SLOT, rem = o - k * AS::SLOT, i = rem >> 8;
+      int o = c * 1024 + lane * 16;
+      asm volatile("" : "+v"(o));   // computed here, not kept live across the chunk loop
+      const int k = o / AS::SLOT, rem = o - k * AS::SLOT, i = rem / AS::SB;
       uint32_t t = tk[0];
 #pragma unroll
       for (int kk = 1; kk < AS::NV; ++kk) t = k == kk ? tk[kk] : t;
       const bool ok = k < nrows && i < n_s;
-      const uint32_t off = ok ? t * (uint32_t)a_row + (uint32_t)(s0 + i) * 256u + (uint32_t)(rem & 255) : 0u;
+      const uint32_t off =
+          ok ? t * (uint32_t)a_row + (uint32_t)(s0 + i) * AS::SB + (uint32_t)(rem % AS::SB) : 0u;
       dma16_lds(p.x, off, lds0 + c * 1024);
     }
   };
@@ -213,14 +221,19 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     const int n_s = s_end - s0;
     uint4 bq[PF][NB];
     ScaleQuads<PF> bsq[NB];
+    ScaleQuads<PF> asq;
 #pragma unroll
     for (int j = 0; j < NB; ++j) bsq[j].load(bsrow[j], s0, s_end, g, true);
+    if (ADT != DT_BF16) asq.load(asrow[0], s0, s_end, g, aval[0]);
     stage_group(0, s0, n_s);
+    const uint8_t* bbase[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bbase[j] = brow[j] + s0 * 64 + 16 * g;
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       if (FULL || i < n_s)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
+        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 64);
     __builtin_amdgcn_sched_barrier(0);
     // the copies were issued before the PF*NB weight loads: once at most that many loads are
     // outstanding, the staged rows are in LDS
@@ -233,23 +246,21 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
         stage_group(q, s0, n_s);
         wait_vm<0>();
       }
+      // a row of this group reads its slot, any other row the zero block (step stride 0)
       const bool in = ((mask16 >> r16) & 1u) && (int)my_j / AS::NV == q;
-      const uint8_t* abase = xs + (in ? ((int)my_j % AS::NV) * AS::SLOT : AS::ZERO) + 64 * g;
-      const int astep = in ? 256 : 0;
+      const uint8_t* abase = xs + (in ? ((int)my_j % AS::NV) * AS::SLOT : AS::ZERO);
+      const int astep = in ? AS::SB : 0;
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
         if (FULL || i < n_s) {
-          AOperand<DT_BF16> A;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const uint4 v = *reinterpret_cast<const uint4*>(abase + i * astep + 16 * jj);
-            A.a[jj] = as_bf16x8(v.x, v.y, v.z, v.w);
-          }
+          AOperand<ADT> A;
+          A.load_lds(abase + i * astep, g);
           uint32_t bs[NB];
 #pragma unroll
           for (int j = 0; j < NB; ++j) bs[j] = bsq[j].get(i, r16, g);
+          const uint32_t as = ADT == DT_BF16 ? 0u : asq.get(i, r16, g);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[0][j] = A.mma(bq[i][j], bs[j], 0u, acc[0][j]);
+          for (int j = 0; j < NB; ++j) acc[0][j] = A.mma(bq[i][j], bs[j], as, acc[0][j]);
         }
       }
     } while (++q < ngroups);
