@@ -48,12 +48,14 @@ __global__ __launch_bounds__(THREADS, MINW) void stage2_kernel(FusedArgs p, int 
 //
 // out[t, c] = sum over k (ascending) of rowout[row_of[t*topk + k], c], in fp32, rounded to
 // bf16.  Thread = 8 consecutive columns of one token; rows of non-local experts (-1) are skipped.
+// W: the rows were stored without the router weight (grouped Stage2); each is multiplied by
+// topk_w[t*topk + k] in fp32 before it is added.
 
-template <bool F32>
+template <bool F32, bool W = false>
 __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restrict__ rowout,
                                                           const int32_t* __restrict__ row_of,
                                                           uint16_t* __restrict__ out, int T, int topk,
-                                                          int D) {
+                                                          int D, const float* __restrict__ topk_w = nullptr) {
   const int groups = D / 8;
   const int64_t idx = (int64_t)blockIdx.x * THREADS + threadIdx.x;
   if (idx >= (int64_t)T * groups) return;
@@ -84,17 +86,25 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
       }
     } else {
       uint4 q[KG];
+      float wk[KG];
 #pragma unroll
-      for (int u = 0; u < KG; ++u)
+      for (int u = 0; u < KG; ++u) {
         q[u] = r[u] >= 0 ? *reinterpret_cast<const uint4*>(rowout + ((size_t)r[u] * D + c) * 2)
                          : uint4{0u, 0u, 0u, 0u};
+        if (W) wk[u] = r[u] >= 0 ? topk_w[(int64_t)t * topk + k0 + u] : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < KG; ++u) {
         const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          sum[2 * h] += __uint_as_float(w[h] << 16);
-          sum[2 * h + 1] += __uint_as_float(w[h] & 0xFFFF0000u);
+          if (W) {
+            sum[2 * h] += wk[u] * __uint_as_float(w[h] << 16);
+            sum[2 * h + 1] += wk[u] * __uint_as_float(w[h] & 0xFFFF0000u);
+          } else {
+            sum[2 * h] += __uint_as_float(w[h] << 16);
+            sum[2 * h + 1] += __uint_as_float(w[h] & 0xFFFF0000u);
+          }
         }
       }
     }
@@ -315,6 +325,8 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
   const unsigned gridc = (unsigned)((nthreads + THREADS - 1) / THREADS);
   if (ADT == DT_BF16)
     combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
+  else if (tiled2)   // grouped Stage2 rows carry no router weight
+    combine_kernel<false, true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, a.topk_w);
   else
     combine_kernel<false><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
   return hipGetLastError();

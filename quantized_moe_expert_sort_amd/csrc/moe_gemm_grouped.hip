@@ -70,6 +70,7 @@ __device__ __forceinline__ int group_size(int len) {
   return (len + ng - 1) / ng;
 }
 
+static_assert(GROUP_LDS_TILES % GROUP_THREADS == 0, "whole loads per thread");
 __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __restrict__ expert_ids,
                                                               const int32_t* __restrict__ num_tiles_p,
                                                               int cap, int2* __restrict__ groups,
@@ -78,8 +79,20 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __r
   __shared__ int tmp[GROUP_THREADS / WAVE + 1];
   const int n = min(*num_tiles_p, cap);
   const bool in_lds = n <= GROUP_LDS_TILES;
-  if (in_lds)
-    for (int i = threadIdx.x; i < n; i += GROUP_THREADS) lds_e[i] = expert_ids[i];
+  if (in_lds) {   // GROUP_LDS_TILES / GROUP_THREADS loads per thread, all issued before the stores
+    constexpr int PER = GROUP_LDS_TILES / GROUP_THREADS;
+    int v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = threadIdx.x + u * GROUP_THREADS;
+      v[u] = i < n ? expert_ids[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = threadIdx.x + u * GROUP_THREADS;
+      if (i < n) lds_e[i] = v[u];
+    }
+  }
   __syncthreads();
   auto E = [&](int i) { return in_lds ? lds_e[i] : expert_ids[i]; };
   const int per = (n + GROUP_THREADS - 1) / GROUP_THREADS;
@@ -143,14 +156,19 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t ld
 
 // Wait until at most n of this wave's vector memory operations are outstanding (they complete
 // in issue order), then meet the other waves.  lgkmcnt(0): this wave's LDS accesses are done,
-// so a buffer may be refilled once every wave has passed.  n >= 63 waits for nothing.
+// so a buffer may be refilled once every wave has passed.  n = 63 waits for nothing; n > 63
+// waits for everything.
 __device__ __forceinline__ void wait_and_barrier(int n) {
   switch (n) {
 #define MOE_WB(k) case k: asm volatile("s_waitcnt vmcnt(" #k ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     MOE_WB(1) MOE_WB(2) MOE_WB(3) MOE_WB(4) MOE_WB(5) MOE_WB(6) MOE_WB(7) MOE_WB(8) MOE_WB(9)
     MOE_WB(10) MOE_WB(11) MOE_WB(12) MOE_WB(13) MOE_WB(14) MOE_WB(15) MOE_WB(16) MOE_WB(17)
     MOE_WB(18) MOE_WB(19) MOE_WB(20) MOE_WB(21) MOE_WB(22) MOE_WB(23) MOE_WB(24) MOE_WB(25)
-    MOE_WB(26) MOE_WB(27) MOE_WB(28) MOE_WB(29) MOE_WB(30) MOE_WB(31)
+    MOE_WB(26) MOE_WB(27) MOE_WB(28) MOE_WB(29) MOE_WB(30) MOE_WB(31) MOE_WB(32) MOE_WB(33)
+    MOE_WB(34) MOE_WB(35) MOE_WB(36) MOE_WB(37) MOE_WB(38) MOE_WB(39) MOE_WB(40) MOE_WB(41)
+    MOE_WB(42) MOE_WB(43) MOE_WB(44) MOE_WB(45) MOE_WB(46) MOE_WB(47) MOE_WB(48) MOE_WB(49)
+    MOE_WB(50) MOE_WB(51) MOE_WB(52) MOE_WB(53) MOE_WB(54) MOE_WB(55) MOE_WB(56) MOE_WB(57)
+    MOE_WB(58) MOE_WB(59) MOE_WB(60) MOE_WB(61) MOE_WB(62)
 #undef MOE_WB
     case 63: asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
@@ -500,6 +518,214 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
   }
 }
 
+// ---------------------------------------------------------------- grouped Stage2
+//
+// Stage2 items stage nothing in LDS.  The MFMA takes the weight rows as its first operand and
+// the intermediate rows as its second, so lane (r, g) of a 16 x 16 accumulator holds four
+// consecutive output columns of row r; the weight rows of a wave's four fragments are
+// interleaved (row m of fragment j is output column 32 (j / 2) + 8 (m / 4) + 4 (j % 2) + m % 4 of
+// the wave's 64), so a lane ends up with two runs of 8 consecutive columns of one row, written
+// as two 16-byte stores that cover 64 contiguous bytes per row across the lane groups.  The operand buffers are free as soon as the K loop ends: the loader waves issue the
+// next item's first P-1 steps before storing, and one item's output drains while the next
+// item's operands arrive (the loaders' waits count the stores issued after those copies).  The
+// rows are stored without the router weight; the combine applies it.
+
+template <int ADT>
+__device__ __forceinline__ v4f mfma_w_x(const v8i& w, const v8i& x, const v4f& c, uint32_t sw, uint32_t sx) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, c, MFMA_FMT_FP4,
+                                                          ADT == DT_FP8 ? MFMA_FMT_FP8 : MFMA_FMT_FP4, 0, sw, 0, sx);
+}
+
+// scalar (constant-cache) load of a wave-uniform address: counted by lgkmcnt, not vmcnt
+__device__ __forceinline__ int ld_const(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+
+template <int ADT>
+__global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p, const int2* __restrict__ groups,
+                                                                     const int32_t* __restrict__ num_groups,
+                                                                     int n_nblk) {
+  using F = GFmt<ADT>;
+  constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[P * F::BUF];
+
+  const int D = p.D, I = p.I;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
+  const bool loader = wave < NLOAD;
+  const int lw = wave & (NLOAD - 1);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+  const int S = I / 128;
+  const uint32_t lds0 = lds_addr(lds);
+  const size_t a_rowbytes = (size_t)I * KA / 128;
+
+  const int ng = ld_const(num_groups);
+  const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
+  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_nblk;
+
+  struct Src {
+    const uint8_t *a, *as, *b, *bs;
+    uint32_t a_off[F::A_IPL], b_off[F::B_IPL], as_off, bs_off;
+    int n_ai, rows_used, row_base, nb, per_step;
+    bool as_on;
+  };
+  // copy sources of item `local`: A the group's intermediate rows (rows past the group read its
+  // first row; their results are not stored), B output rows [nb*BNW, nb*BNW + BNW) of w2
+  auto make = [&](int local, Src& q) {
+    const int gl = local / n_nblk;
+    q.nb = local - gl * n_nblk;
+    const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
+    const int tile0 = ld_const(gp), ntiles = ld_const(gp + 1);
+    q.rows_used = ntiles * 32;
+    q.row_base = tile0 * 32;
+    const int e = ld_const(p.expert_ids + tile0);
+    q.a = p.inter + (size_t)q.row_base * a_rowbytes;
+    q.as = p.inter_s + (size_t)q.row_base * (I / 32);
+    q.b = p.w2 + (size_t)e * D * (I / 2);
+    q.bs = p.w2s + (size_t)e * D * (I / 32);
+    int n_ai = 0;
+#pragma unroll
+    for (int i = 0; i < F::A_IPL; ++i) {
+      const int j = i * NLOAD + lw;
+      const int qq = j * WAVE + lane;
+      const int row = qq / ACPR, part = swz_slot<ACPR>(row, qq % ACPR) - row * ACPR;
+      q.a_off[i] = (uint32_t)(row < q.rows_used ? row : 0) * (uint32_t)a_rowbytes + part * 16;
+      n_ai += j * F::ROWS_PER_AI < q.rows_used;
+    }
+#pragma unroll
+    for (int i = 0; i < F::B_IPL; ++i) {
+      const int j = i * NLOAD + lw;
+      const int qq = j * WAVE + lane;
+      const int row = qq / 4, part = swz_slot<4>(row, qq % 4) - row * 4;
+      q.b_off[i] = (uint32_t)(q.nb * BNW + row) * (uint32_t)(I / 2) + part * 16;
+    }
+    const int sc_row = lw * WAVE + lane;
+    q.as_on = lw * WAVE < q.rows_used;
+    q.as_off = (uint32_t)(sc_row < q.rows_used ? sc_row : 0) * (uint32_t)(I / 32);
+    q.bs_off = (uint32_t)(q.nb * BNW + sc_row) * (uint32_t)(I / 32);
+    q.n_ai = n_ai;
+    q.per_step = n_ai + F::B_IPL + (q.as_on ? 1 : 0) + 1;
+  };
+  auto issue = [&](const Src& q, int s, int buf) {
+    const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * F::BUF);
+    const uint8_t* ab = q.a + s * KA;
+    const uint8_t* bb = q.b + s * 64;
+#pragma unroll
+    for (int i = 0; i < F::A_IPL; ++i)
+      if (i < q.n_ai) dma16(ab, q.a_off[i], L + (i * NLOAD + lw) * 1024);
+#pragma unroll
+    for (int i = 0; i < F::B_IPL; ++i)
+      dma16(bb, q.b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
+    if (q.as_on) dma4(q.as + s * 4, q.as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
+    dma4(q.bs + s * 4, q.bs_off, L + F::A_BYTES + F::B_BYTES + BMW * 4 + lw * 256);
+  };
+
+  const int arow0 = 128 * wm;
+  Src cur, nxt;
+  int local = local0;
+  if (local < items_here) {
+    make(local, cur);
+    if (loader) {
+#pragma unroll
+      for (int q = 0; q < P - 1; ++q)
+        if (q < S) issue(cur, q, q);
+    }
+  }
+  int n_st = 0;   // stores this wave issued after the current item's first copies
+  for (; local < items_here; local += stride) {
+    const bool has_next = local + stride < items_here;
+    if (has_next) make(local + stride, nxt);
+    const int n_af = max(0, min(MFW, (cur.rows_used - arow0) / 16));
+
+    auto run = [&](auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+      v4f acc[NA > 0 ? NA : 1][NFW];
+#pragma unroll
+      for (int f = 0; f < NA; ++f)
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+      auto compute = [&](int buf) {
+        const uint8_t* la = lds + buf * F::BUF;
+        const uint8_t* lb = la + F::A_BYTES;
+        const uint32_t* las = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
+        const uint32_t* lbs = las + BMW;
+        v8i wop[NFW];
+        uint32_t wsc[NFW];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          const int br = 64 * wn + (j >> 1) * 32 + 8 * (r16 >> 2) + 4 * (j & 1) + (r16 & 3);
+          wop[j] = fp4_operand_lo(*reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16));
+          wsc[j] = (lbs[br] >> (8 * g)) & 0xFFu;
+        }
+        auto load_x = [&](int f, v8i& xop, uint32_t& xsc) {
+          const int ar = arow0 + 16 * f + r16;
+          if (ADT == DT_FP8) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, g) * 16);
+            const uint4 hi = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, 4 + g) * 16);
+            xop = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          } else {
+            xop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
+          }
+          xsc = (las[ar] >> (8 * g)) & 0xFFu;
+        };
+        v8i x_cur;
+        uint32_t xs_cur;
+        load_x(0, x_cur, xs_cur);
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+          v8i x_nxt = x_cur;
+          uint32_t xs_nxt = xs_cur;
+          if (f + 1 < NA) load_x(f + 1, x_nxt, xs_nxt);
+#pragma unroll
+          for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xs_cur);
+          __builtin_amdgcn_sched_barrier(0);
+          x_cur = x_nxt;
+          xs_cur = xs_nxt;
+        }
+      };
+
+      for (int s = 0; s < S; ++s) {
+        // a loader's copies of step s are done once at most (those issued after them) remain:
+        // the later steps' copies, and for the first P-1 steps also the previous item's stores
+        wait_and_barrier(loader ? cur.per_step * min(S - 1 - s, P - 2) + (s < P - 1 ? n_st : 0) : 63);
+        if (loader && s + P - 1 < S) issue(cur, s + P - 1, (s + P - 1) % P);
+        if (NA > 0) compute(s % P);
+      }
+      lds_barrier();                                      // every operand read of the item is done
+      if (loader && has_next) {
+#pragma unroll
+        for (int q = 0; q < P - 1; ++q)
+          if (q < S) issue(nxt, q, q);
+      }
+      // row arow0 + 16 f + r16, output columns 64 wn + 8 g .. + 7 and 64 wn + 32 + 8 g .. + 7 of
+      // column block nb: each store instruction covers 64 contiguous bytes of 16 rows
+      uint8_t* obase = p.rowout + (((size_t)cur.row_base + arow0 + r16) * D + (size_t)cur.nb * BNW + 64 * wn + 8 * g) * 2;
+#pragma unroll
+      for (int f = 0; f < NA; ++f) {
+        uint32_t d[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          d[k] = (uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1)]) |
+                 ((uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1) + 1]) << 16);
+        uint8_t* o = obase + (size_t)16 * f * D * 2;
+        *reinterpret_cast<uint4*>(o) = uint4{d[0], d[1], d[2], d[3]};
+        *reinterpret_cast<uint4*>(o + 64) = uint4{d[4], d[5], d[6], d[7]};
+      }
+      n_st = 2 * NA;
+    };
+    switch (n_af) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 4: run(std::integral_constant<int, 4>{}); break;
+      case 6: run(std::integral_constant<int, 6>{}); break;
+      default: run(std::integral_constant<int, 8>{}); break;
+    }
+    cur = nxt;
+  }
+}
+
 int g_num_cus = 0;
 
 int num_cus() {
@@ -518,7 +744,7 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
   const int n_nblk = STAGE == 1 ? (2 * a.I) / BNW : a.D / BNW;
   const unsigned grid = (unsigned)(num_cus() / 8 * 8);    // one workgroup per CU, a multiple of 8
   if (STAGE == 2)
-    grouped_gemm_kernel<ADT, 2, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+    grouped_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   else if (a.act == ACT_SITUV2)
     grouped_gemm_kernel<ADT, 1, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   else

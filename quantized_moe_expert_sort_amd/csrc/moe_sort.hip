@@ -283,12 +283,20 @@ __global__ __launch_bounds__(SCAN_THREADS) void sort_scan_kernel(int* __restrict
   extern __shared__ int smem[];
   int* pos = smem;                       // [E]
   int* tmp = pos + E;                    // [SCAN_THREADS / WAVE + 1]
+  // the counts of SB chunks are loaded together, then turned into exclusive offsets: a memory
+  // latency per SB chunks instead of one per chunk
+  constexpr int SB = 16;
   for (int e = threadIdx.x; e < E; e += SCAN_THREADS) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = hist[(int64_t)c * E + e];
-      hist[(int64_t)c * E + e] = run;
-      run += h;
+    for (int c0 = 0; c0 < nchunks; c0 += SB) {
+      int h[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) h[u] = c0 + u < nchunks ? hist[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        if (c0 + u < nchunks) hist[(int64_t)(c0 + u) * E + e] = run;
+        run += h[u];
+      }
     }
     pos[e] = run;
   }
@@ -297,7 +305,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void sort_scan_kernel(int* __restrict
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += SCAN_THREADS) {
     const int first = pos[e];
-    for (int c = 0; c < nchunks; ++c) hist[(int64_t)c * E + e] += first;
+    for (int c0 = 0; c0 < nchunks; c0 += SB) {
+      int h[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) h[u] = c0 + u < nchunks ? hist[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        if (c0 + u < nchunks) hist[(int64_t)(c0 + u) * E + e] = h[u] + first;
+    }
   }
 }
 
