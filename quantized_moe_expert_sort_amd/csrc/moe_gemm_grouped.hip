@@ -426,24 +426,27 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
             }
             const uint32_t amax =
                 row16_max_u32(max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu));
-            uint32_t code[2], sbyte;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              code[h] = ADT == DT_FP8 ? encode_in_block<Fp8Fmt>(__float_as_uint(y[h]), amax, &sbyte)
-                                      : encode_in_block<Fp4Fmt>(__float_as_uint(y[h]), amax, &sbyte);
-            // every lane writes its own column (32 wn + 16 h + r16 of the block); for fp4 both
-            // lanes of a nibble pair write the same byte, and all 16 lanes the same scale byte
+            // the 1x32 rule with the hardware converts: an even lane encodes its column and the
+            // next one (the odd lane's value comes over DPP); an Inf / NaN block gets scale 255
+            // and zero codes
+            const bool bad = amax >= 0x7F800000u;
+            const int sexp = block_sexp_any(bad ? 0u : amax, ADT == DT_FP8 ? Fp8Fmt::EMAX : Fp4Fmt::EMAX);
+            const float scale = e8m0_scale_float(sexp);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+              const float yn = __uint_as_float(lane_xor1(__float_as_uint(y[h])));
               const int c = 32 * wn + 16 * h + r16;
-              if (ADT == DT_FP8) {
-                st_codes[row * F::OBS + c] = (uint8_t)code[h];
-              } else {
-                const uint32_t partner = lane_xor1(code[h]);
-                st_codes[row * F::OBS + c / 2] = (uint8_t)((r16 & 1) ? (partner | (code[h] << 4)) : (code[h] | (partner << 4)));
+              if ((r16 & 1) == 0) {
+                if (ADT == DT_FP8) {
+                  const uint32_t pr = bad ? 0u : encode_pair_fp8_hw(y[h], yn, sexp);
+                  *reinterpret_cast<uint16_t*>(st_codes + row * F::OBS + c) = (uint16_t)pr;
+                } else {
+                  const uint32_t pr = bad ? 0u : encode_pair_fp4_hw(y[h], yn, scale);
+                  st_codes[row * F::OBS + c / 2] = (uint8_t)pr;
+                }
               }
             }
-            st_scales[row * 4 + wn] = (uint8_t)sbyte;
+            st_scales[row * 4 + wn] = (uint8_t)(bad ? 255u : (uint32_t)(sexp + 127));
           }
         }
         lds_barrier();

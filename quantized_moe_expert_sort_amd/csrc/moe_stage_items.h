@@ -316,23 +316,27 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
       if (valid && (col & 1) == 0)
         st<COH>(reinterpret_cast<uint32_t*>(p.inter + ((size_t)R * I + ocol) * 2), h | (h1 << 16));
     } else {
-      uint32_t sb, word;
+      // the 1x32 rule over the 32 lanes of a block with the hardware converts: an even lane
+      // encodes its column and the next (the odd lane's value comes over DPP), then the pairs
+      // are gathered into 4-byte stores
+      const uint32_t bits = __float_as_uint(y);
+      const uint32_t amax = halfwave_max_u32(bits & 0x7FFFFFFFu);
+      const bool bad = amax >= 0x7F800000u;                // Inf / NaN: scale 255, zero codes
+      const int sexp = block_sexp_any(bad ? 0u : amax, ADT == DT_FP8 ? Fp8Fmt::EMAX : Fp4Fmt::EMAX);
+      const float yn = __uint_as_float(lane_xor1(bits));
       if (ADT == DT_FP8) {
-        const uint32_t c = block_encode_lane<Fp8Fmt>(y, &sb);
-        const uint32_t c1 = (uint32_t)__shfl_down((int)c, 1, WAVE);
-        const uint32_t c2 = (uint32_t)__shfl_down((int)c, 2, WAVE);
-        const uint32_t c3 = (uint32_t)__shfl_down((int)c, 3, WAVE);
-        word = c | (c1 << 8) | (c2 << 16) | (c3 << 24);
+        const uint32_t pr = bad ? 0u : encode_pair_fp8_hw(y, yn, sexp);
+        const uint32_t word = pr | ((uint32_t)__shfl_down((int)pr, 2, WAVE) << 16);
         if (valid && (col & 3) == 0) st<COH>(reinterpret_cast<uint32_t*>(p.inter + (size_t)R * I + ocol), word);
       } else {
-        const uint32_t c = block_encode_lane<Fp4Fmt>(y, &sb);
-        const uint32_t p2 = c | ((uint32_t)__shfl_down((int)c, 1, WAVE) << 4);
-        const uint32_t p4 = p2 | ((uint32_t)__shfl_down((int)p2, 2, WAVE) << 8);
-        word = p4 | ((uint32_t)__shfl_down((int)p4, 4, WAVE) << 16);
+        const uint32_t pb = bad ? 0u : encode_pair_fp4_hw(y, yn, e8m0_scale_float(sexp));
+        const uint32_t p2 = pb | ((uint32_t)__shfl_down((int)pb, 2, WAVE) << 8);
+        const uint32_t word = p2 | ((uint32_t)__shfl_down((int)p2, 4, WAVE) << 16);
         if (valid && (col & 7) == 0)
           st<COH>(reinterpret_cast<uint32_t*>(p.inter + (size_t)R * (I / 2) + ocol / 2), word);
       }
-      if (valid && (col & 31) == 0) st<COH>(p.inter_s + (size_t)R * (I / 32) + ocol / 32, (uint8_t)sb);
+      if (valid && (col & 31) == 0)
+        st<COH>(p.inter_s + (size_t)R * (I / 32) + ocol / 32, (uint8_t)(bad ? 255u : (uint32_t)(sexp + 127)));
     }
   }
   return true;
