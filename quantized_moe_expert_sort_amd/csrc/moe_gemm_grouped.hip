@@ -10,11 +10,11 @@
 // w + 4 share a SIMD and own the two row halves, so every SIMD does the same work whatever
 // the group's row count.
 //
-// Operand staging: per 128-deep K step the A rows (gathered activations or intermediate rows),
-// the B rows (fp4 weights) and the e8m0 scale dwords of both are copied global -> LDS by the
-// load-to-LDS instructions (global_load_lds_dwordx4 / _dword: lane l of a wave instruction
-// writes bytes [16l, 16l+16) (or [4l, 4l+4)) after the wave's LDS address in m0), P steps in
-// flight (P LDS buffers), one barrier per step.  The copies are issued from inline assembly,
+// Operand staging: per 128-deep K step the A rows (gathered activations or intermediate rows)
+// and the B rows (fp4 weights) are copied global -> LDS by the load-to-LDS instructions
+// (global_load_lds_dwordx4 / _dword: lane l of a wave instruction writes bytes [16l, 16l+16)
+// (or [4l, 4l+4)) after the wave's LDS address in m0), P steps in flight (P LDS buffers), one
+// barrier per step; Stage1 copies the e8m0 scales of a row 16 bytes (four K steps) at a time.  The copies are issued from inline assembly,
 // so the only waits on them are the explicit vmcnt waits of the pipeline.  The 16-byte chunks
 // of a row are stored XOR-swizzled (chunk p of row r at position p ^ swz(r)), so the 16 lanes
 // that read one chunk column of 16 rows for a matrix-core operand hit distinct LDS banks.
@@ -28,8 +28,8 @@
 // epilogue): a wave's B rows are [32 gate rows | the matching 32 up rows], so g and u of one
 // output sit in the same lane; y = act(g, u) is re-encoded per 32-column block (PR 4463 "Three
 // tuner defects" item 2: fused fp4 stage1 output) with the block maximum reduced over 16 lanes.
-// Stage2 epilogue: the row result times the router weight, stored as bf16 per routed row for the
-// gather combine.
+// Stage2 (grouped_stage2_kernel below) stores bf16 rows without the router weight; the combine
+// applies it.
 #include "moe_kernels.h"
 #include "moe_operands.h"
 
@@ -49,7 +49,6 @@ constexpr int BMW = GT * 32;                  // rows per group: 256
 constexpr int BNW = 256;                      // weight rows per column block
 constexpr int MFW = BMW / WM / 16;            // 16-row A fragments per wave: 8
 constexpr int NFW = BNW / WN / 16;            // 16-row B fragments per wave: 4
-constexpr int STG_STRIDE = BNW * 2 + 16;      // LDS row stride of the staged Stage2 output tile
 static_assert(WM * WN == GWAVES, "wave grid");
 
 // ---------------------------------------------------------------- tile groups
@@ -210,6 +209,7 @@ struct GFmt {
   static constexpr int KA = ADT == DT_FP8 ? 128 : 64;     // A bytes per row per K step
   static constexpr int ACPR = KA / 16;                    // 16-byte chunks per A row
   static constexpr int P = ADT == DT_FP8 ? 3 : 4;         // LDS buffers = K steps in flight + 1
+  static constexpr int AD = ADT == DT_FP8 ? 2 : 3;        // A fragments read ahead of the MFMAs
   static constexpr int A_BYTES = BMW * KA;
   static constexpr int B_BYTES = BNW * 64;
   static constexpr int BUF = A_BYTES + B_BYTES + (BMW + BNW) * 4;
@@ -220,19 +220,37 @@ struct GFmt {
   static constexpr int OBS = OB + 16;                     // their LDS row stride
 };
 
-template <int ADT, int STAGE, int ACT>
-__global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, const int2* __restrict__ groups,
-                                                                  const int32_t* __restrict__ num_groups,
-                                                                  int n_nblk) {
+// Stage1 LDS: P operand buffers [A tile | B tile | A scale dwords (fp8)], then two slots of
+// per-row scale chunks.  16 bytes of a row's e8m0 scales cover four K steps (512 columns), so a
+// row's scales arrive with one 16-byte copy per four steps instead of a 4-byte copy per step
+// (a copy instruction whose 64 lanes touch 64 different cache lines costs the memory pipeline
+// as much as one that moves a kilobyte).  fp4 activations take A and B scales in chunks; the
+// fp8 A tile leaves room for the B chunks only.
+template <int ADT>
+struct S1Fmt {
   using F = GFmt<ADT>;
+  static constexpr bool AW = ADT == DT_FP4;               // A scales in chunks
+  static constexpr int BUF = F::A_BYTES + F::B_BYTES + (AW ? 0 : BMW * 4);
+  static constexpr int A_SLOT = AW ? BMW * 16 : 0;
+  static constexpr int SLOT = A_SLOT + BNW * 16;
+  static constexpr int BYTES = F::P * BUF + 2 * SLOT;
+};
+
+template <int ADT, int ACT>
+__global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p, const int2* __restrict__ groups,
+                                                                    const int32_t* __restrict__ num_groups,
+                                                                    int n_nblk) {
+  using F = GFmt<ADT>;
+  using L1 = S1Fmt<ADT>;
   constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P;
+  constexpr bool AW = L1::AW;
   static_assert(F::A_IPL * NLOAD * 1024 == F::A_BYTES && F::B_IPL * NLOAD * 1024 == F::B_BYTES, "copy split");
   static_assert(BMW == NLOAD * WAVE && BNW == NLOAD * WAVE, "one scale copy of each operand per loader");
-  static_assert(BMW * STG_STRIDE <= P * F::BUF && BMW * (F::OBS + 4) <= P * F::BUF, "staging fits");
+  static_assert(BMW * (F::OBS + 4) <= P * L1::BUF, "staging fits");
+  static_assert(P <= 5, "a chunk slot is refilled only after the four steps of its previous chunk");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[P * F::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L1::BYTES];
   __shared__ int lds_v[BMW];
-  __shared__ float lds_w[BMW];
 
   const int TK = p.T * p.topk, D = p.D, I = p.I;
   const int lane = threadIdx.x & (WAVE - 1);
@@ -241,9 +259,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
   const int lw = wave & (NLOAD - 1);
   const int r16 = lane & 15, g = lane >> 4;
   const int wm = wave / WN, wn = wave % WN;
-  const int K = STAGE == 1 ? D : I;
+  const int K = D;                                        // a multiple of 512: whole chunks
   const int S = K / 128;
   const uint32_t lds0 = lds_addr(lds);
+  const uint32_t slot0 = lds0 + P * L1::BUF;
 
   // groups gi = xcd, xcd + 8, ... run on XCD xcd; item (group, column block)
   const int ng = *num_groups;
@@ -259,33 +278,24 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
     const int row_base = tile0 * 32;                      // first layout row of the group
     if (loader) {
       const int r = threadIdx.x;                          // < BMW
-      const int v = r < rows_used ? p.sorted_ids[row_base + r] : TK;
-      lds_v[r] = v;
-      if (STAGE == 2) lds_w[r] = (unsigned)v < (unsigned)TK ? p.topk_w[v] : 0.f;
+      lds_v[r] = r < rows_used ? p.sorted_ids[row_base + r] : TK;
     }
     lds_barrier();
 
-    // ---- copy sources.  A: stage1 gathered x rows (padding rows read token 0, their results
-    // are never stored), stage2 the group's intermediate rows.  B: stage1 [gate NI | up NI]
-    // rows of column block nb (NI = BNW/2), stage2 BNW output rows.
+    // ---- copy sources.  A: the gathered x rows (padding rows read token 0, their results are
+    // never stored).  B: [gate NI | up NI] rows of column block nb (NI = BNW/2).
     const size_t a_rowbytes = (size_t)K * KA / 128;
-    const uint8_t* a_base = STAGE == 1 ? p.x : p.inter + (size_t)row_base * a_rowbytes;
-    const uint8_t* as_base = STAGE == 1 ? p.xs : p.inter_s + (size_t)row_base * (K / 32);
-    const uint8_t* b_base = STAGE == 1 ? p.w1 + (size_t)e * 2 * I * (D / 2) : p.w2 + (size_t)e * D * (I / 2);
-    const uint8_t* bs_base = STAGE == 1 ? p.w1s + (size_t)e * 2 * I * (D / 32) : p.w2s + (size_t)e * D * (I / 32);
+    const uint8_t* a_base = p.x;
+    const uint8_t* as_base = p.xs;
+    const uint8_t* b_base = p.w1 + (size_t)e * 2 * I * (D / 2);
+    const uint8_t* bs_base = p.w1s + (size_t)e * 2 * I * (D / 32);
     auto b_row = [&](int r) -> int {                      // weight row within the expert
-      if (STAGE == 1) {
-        constexpr int NI = BNW / 2;
-        return r < NI ? nb * NI + r : I + nb * NI + (r - NI);
-      }
-      return nb * BNW + r;
+      constexpr int NI = BNW / 2;
+      return r < NI ? nb * NI + r : I + nb * NI + (r - NI);
     };
-    auto a_src_index = [&](int row) -> uint32_t {        // source row of A row `row`
-      if (STAGE == 1) {
-        const int v = lds_v[row];
-        return (uint32_t)((unsigned)v < (unsigned)TK ? v / p.topk : 0);
-      }
-      return (uint32_t)(row < rows_used ? row : 0);
+    auto a_src_index = [&](int row) -> uint32_t {        // token row of A row `row`
+      const int v = lds_v[row];
+      return (uint32_t)((unsigned)v < (unsigned)TK ? v / p.topk : 0);
     };
     // loader lw issues tile instructions j = i * NLOAD + lw (A rows [j * ROWS_PER_AI, ...));
     // A instructions wholly past the group's rows are not issued
@@ -307,16 +317,25 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
       const int row = q / 4, part = swz_slot<4>(row, q % 4) - row * 4;
       b_off[i] = (uint32_t)b_row(row) * (uint32_t)(K / 2) + part * 16;
     }
-    // scale dwords: loader lw copies those of A rows and of B rows [64 lw, 64 lw + 64)
+    // scales: loader lw copies those of A rows and of B rows [64 lw, 64 lw + 64)
     const int sc_row = lw * WAVE + lane;
     const bool as_on = lw * WAVE < rows_used;
     const uint32_t as_off = a_src_index(sc_row) * (uint32_t)(K / 32);
     const uint32_t bs_off = (uint32_t)b_row(sc_row) * (uint32_t)(K / 32);
-    const int per_step = n_ai + F::B_IPL + (as_on ? 1 : 0) + 1;
+    // copy instructions a loader issues for step s: the chunks travel with steps 0, 4, 8, ...
+    const int n_data = n_ai + F::B_IPL + (!AW && as_on ? 1 : 0);
+    const int n_chunk = 1 + (AW && as_on ? 1 : 0);
 
-    // per step the K advance goes into the (scalar) global base; lane offsets stay fixed
+    // per step the K advance goes into the (scalar) global base; lane offsets stay fixed.  The
+    // chunk copies are issued first, so the wait for a step's tiles covers them.
     auto issue = [&](int s, int buf) {
-      const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * F::BUF);
+      if ((s & 3) == 0) {
+        const uint32_t C = __builtin_amdgcn_readfirstlane(slot0 + ((s >> 2) & 1) * L1::SLOT);
+        const int cb = (s >> 2) * 16;
+        if (AW && as_on) dma16(as_base + cb, as_off, C + lw * 1024);
+        dma16(bs_base + cb, bs_off, C + L1::A_SLOT + lw * 1024);
+      }
+      const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * L1::BUF);
       const uint8_t* ab = a_base + s * KA;
       const uint8_t* bb = b_base + s * 64;
 #pragma unroll
@@ -325,16 +344,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
 #pragma unroll
       for (int i = 0; i < F::B_IPL; ++i)
         dma16(bb, b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
-      if (as_on) dma4(as_base + s * 4, as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
-      dma4(bs_base + s * 4, bs_off, L + F::A_BYTES + F::B_BYTES + BMW * 4 + lw * 256);
+      if (!AW && as_on) dma4(as_base + s * 4, as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
     };
 
-    // the wave's B fragment rows: stage1 gate rows [32wn, 32wn+32) and the same up rows;
-    // stage2 rows [64wn, 64wn+64)
-    auto b_frag_row = [&](int j) -> int {
-      if (STAGE == 1) return j < 2 ? 32 * wn + 16 * j : BNW / 2 + 32 * wn + 16 * (j - 2);
-      return 64 * wn + 16 * j;
-    };
+    // the wave's B fragment rows: gate rows [32wn, 32wn+32) and the same up rows
+    auto b_frag_row = [&](int j) -> int { return j < 2 ? 32 * wn + 16 * j : BNW / 2 + 32 * wn + 16 * (j - 2); };
     const int arow0 = 128 * wm;                           // the wave's first A row
     // A fragments of this wave that hold group rows: rows_used is a multiple of 32, so 0, 2, 4,
     // 6 or 8; the MFMA loop is instantiated per count (no per-fragment branches inside it)
@@ -348,21 +362,24 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
 #pragma unroll
         for (int j = 0; j < NFW; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-      auto compute = [&](int buf) {
-        const uint8_t* la = lds + buf * F::BUF;
+      auto compute = [&](int s) {
+        const uint8_t* la = lds + (s % P) * L1::BUF;
         const uint8_t* lb = la + F::A_BYTES;
         const uint32_t* las = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
-        const uint32_t* lbs = las + BMW;
+        // this step's scale dword of row r in the chunk slot: bytes [16 r + kq, 16 r + kq + 4)
+        const uint8_t* slot = lds + P * L1::BUF + ((s >> 2) & 1) * L1::SLOT;
+        const int kq = (s & 3) * 4;
         v8i bop[NFW];
         uint32_t bsc[NFW];
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
           const int br = b_frag_row(j) + r16;
           bop[j] = fp4_operand_lo(*reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16));
-          bsc[j] = (lbs[br] >> (8 * g)) & 0xFFu;
+          bsc[j] = (*reinterpret_cast<const uint32_t*>(slot + L1::A_SLOT + br * 16 + kq) >> (8 * g)) & 0xFFu;
         }
-        // A fragment f+1 is read from LDS while the MFMAs of fragment f run; the scheduling
-        // barrier keeps the compiler from hoisting every fragment read (register pressure)
+        // A fragment f+AD is read from LDS while the MFMAs of fragment f run (an LDS read
+        // takes longer than the four MFMAs of one fragment); the scheduling barrier keeps the
+        // compiler from hoisting every fragment read (register pressure)
         auto load_a = [&](int f, v8i& aop, uint32_t& asc) {
           const int ar = arow0 + 16 * f + r16;
           if (ADT == DT_FP8) {
@@ -372,24 +389,26 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
           } else {
             aop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
           }
-          asc = (las[ar] >> (8 * g)) & 0xFFu;
+          const uint32_t sw = AW ? *reinterpret_cast<const uint32_t*>(slot + ar * 16 + kq) : las[ar];
+          asc = (sw >> (8 * g)) & 0xFFu;
         };
-        v8i a_cur;
-        uint32_t as_cur;
-        load_a(0, a_cur, as_cur);
+        constexpr int AD = F::AD;
+        v8i aq[AD + 1];
+        uint32_t asq[AD + 1];
+#pragma unroll
+        for (int d = 0; d < AD; ++d)
+          if (d < NA) load_a(d, aq[d], asq[d]);
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
-          v8i a_nxt = a_cur;
-          uint32_t as_nxt = as_cur;
-          if (f + 1 < NA) load_a(f + 1, a_nxt, as_nxt);
+          if (f + AD < NA) load_a(f + AD, aq[(f + AD) % (AD + 1)], asq[(f + AD) % (AD + 1)]);
+          const v8i& a_cur = aq[f % (AD + 1)];
+          const uint32_t as_cur = asq[f % (AD + 1)];
 #pragma unroll
           for (int j = 0; j < NFW; ++j) {
             if (ADT == DT_FP8) acc[f][j] = mfma_fp8_fp4(a_cur, bop[j], acc[f][j], as_cur, bsc[j]);
             else acc[f][j] = mfma_fp4_fp4(a_cur, bop[j], acc[f][j], as_cur, bsc[j]);
           }
           __builtin_amdgcn_sched_barrier(0);
-          a_cur = a_nxt;
-          as_cur = as_nxt;
         }
       };
 
@@ -400,15 +419,20 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
           if (q < S) issue(q, q);
       }
       for (int s = 0; s < S; ++s) {
-        // a loader's copies of step s are done once at most (issued after them) remain
-        wait_and_barrier(loader ? per_step * min(S - 1 - s, P - 2) : 63);
+        // a loader's copies of step s are done once at most those of the later steps in
+        // flight remain
+        int later = 0;
+#pragma unroll
+        for (int t = 1; t <= P - 2; ++t)
+          if (s + t < S) later += n_data + (((s + t) & 3) == 0 ? n_chunk : 0);
+        wait_and_barrier(loader ? later : 63);
         if (loader && s + P - 1 < S) issue(s + P - 1, (s + P - 1) % P);   // refills the buffer of step s-1
-        if (NA > 0) compute(s % P);
+        if (NA > 0) compute(s);
       }
       lds_barrier();                                      // the operand buffers become staging
 
-      // ---- epilogues: the item's output tile is staged in LDS by every wave
-      if (STAGE == 1) {
+      // ---- epilogue: the item's output tile is staged in LDS by every wave
+      {
         uint8_t* st_codes = lds;                          // [BMW][OBS]
         uint8_t* st_scales = lds + BMW * F::OBS;          // [BMW][4]: one byte per 32-column block
         const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
@@ -467,44 +491,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_gemm_kernel(FusedArgs p, 
               const size_t R = (size_t)row_base + row;
               *reinterpret_cast<uint32_t*>(p.inter_s + R * (I / 32) + (size_t)nb * 4) =
                   *reinterpret_cast<const uint32_t*>(st_scales + row * 4);
-            }
-          }
-        }
-      } else {
-        // the weighted bf16 tile; each routed row then leaves as 512 contiguous bytes
-#pragma unroll
-        for (int f = 0; f < NA; ++f) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = arow0 + 16 * f + 4 * g + i;
-            const float w = lds_w[row];
-            uint16_t* srow = reinterpret_cast<uint16_t*>(lds + row * STG_STRIDE) + 64 * wn + r16;
-#pragma unroll
-            for (int j = 0; j < NFW; ++j) srow[16 * j] = f32_to_bf16_rne(acc[f][j][i] * w);
-          }
-        }
-        lds_barrier();
-        if (!loader) {
-          const int t = threadIdx.x - NLOAD * WAVE;
-          constexpr int CPRO = BNW * 2 / 16;              // 16-byte chunks per output row
-          // BATCH chunks are read from LDS before any of them is stored
-          constexpr int NT = (GWAVES - NLOAD) * WAVE, BATCH = 4;
-          for (int c0 = t; c0 < rows_used * CPRO; c0 += NT * BATCH) {
-            uint4 val[BATCH];
-            bool ok[BATCH];
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-              const int c = c0 + NT * u;
-              const int row = min(c / CPRO, BMW - 1), part = c % CPRO;
-              ok[u] = c < rows_used * CPRO && (unsigned)lds_v[row] < (unsigned)TK;
-              val[u] = *reinterpret_cast<const uint4*>(lds + row * STG_STRIDE + part * 16);
-            }
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-              const int c = c0 + NT * u;
-              const int row = c / CPRO, part = c % CPRO;
-              if (ok[u])
-                *reinterpret_cast<uint4*>(p.rowout + (((size_t)row_base + row) * D + (size_t)nb * BNW) * 2 + part * 16) = val[u];
             }
           }
         }
@@ -749,9 +735,9 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
   if (STAGE == 2)
     grouped_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   else if (a.act == ACT_SITUV2)
-    grouped_gemm_kernel<ADT, 1, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+    grouped_stage1_kernel<ADT, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   else
-    grouped_gemm_kernel<ADT, 1, ACT_SILU><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+    grouped_stage1_kernel<ADT, ACT_SILU><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   return hipGetLastError();
 }
 
@@ -759,7 +745,7 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
 
 bool tiled_path_supported(const FusedArgs& a) {
   return a.a_dtype != DT_BF16 && a.block_m == 32 && a.act != ACT_NONE && (2 * a.I) % BNW == 0 &&
-         a.D % BNW == 0;
+         a.D % 512 == 0;   // Stage1 takes whole 16-byte scale chunks; Stage2 needs D % BNW == 0
 }
 
 hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipStream_t s) {
