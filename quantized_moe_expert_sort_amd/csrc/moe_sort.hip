@@ -172,9 +172,11 @@ __device__ __forceinline__ void zero_sync(const SortLayout& L, int64_t first, in
 
 // ---------------------------------------------------------------- one-wave path (rows <= 64)
 //
-// Lane i holds row v = i.  Its rank is the number of lower lanes with the same expert; the
-// tile offset of its expert is the sum of the tile counts of the smaller experts present,
-// read from their group leaders (the lowest lane of each expert group).
+// Lane i holds row v = i.  One pass over the key bits from the top, with a ballot per bit,
+// gives every lane both the set of lanes with its own expert (its rank is the number of lower
+// lanes in it) and the set of lanes with a smaller expert; the tile offset of its expert is
+// the sum of the tile counts held by the group leaders (lowest lane of each expert) in that
+// set, summed bit by bit over ballots of the tile counts.
 
 __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restrict__ ids,
                                                          const float* __restrict__ topk_w, int n,
@@ -183,25 +185,30 @@ __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restri
   const int lane = threadIdx.x;
   int k = -1;
   float w = 0.0f;
-  if (lane < n) {   // both loads issued together: one memory latency before the stores
-    const int id = ids[lane] - expert_begin;
-    if (L.sorted_w) w = topk_w[lane];
-    k = (id >= 0 && id < E) ? id : -1;
+  if (n > 0) {   // both loads issued together (lanes past n re-read row n-1): one memory latency
+    const int src = min(lane, n - 1);
+    const int id = ids[src] - expert_begin;
+    if (L.sorted_w) w = topk_w[src];
+    k = (lane < n && id >= 0 && id < E) ? id : -1;
   }
   const bool valid = k >= 0;
-  const uint64_t same = match_any(k, valid, bits_for(E));
+  uint64_t same = __ballot(valid), less = 0ull;
+  for (int b = bits_for(E) - 1; b >= 0; --b) {
+    const bool bit = (k >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    if (bit) less |= same & ~ones;
+    same &= bit ? ones : ~ones;
+  }
   const uint64_t lt = (1ull << lane) - 1ull;
   const int rank = __popcll(same & lt);
   const int cnt = __popcll(same);
   const bool leader = valid && (same & lt) == 0ull;
   const int tiles = leader ? (cnt + block_m - 1) / block_m : 0;
   int off = 0, total = 0;
-#pragma unroll 8
-  for (int j = 0; j < WAVE; ++j) {
-    const int kj = __builtin_amdgcn_readlane(k, j);
-    const int tj = __builtin_amdgcn_readlane(tiles, j);
-    off += (kj < k) ? tj : 0;
-    total += tj;
+  for (int t = 0; (1 << t) <= (WAVE + block_m - 1) / block_m; ++t) {   // bits of a tile count
+    const uint64_t tb = __ballot((tiles >> t) & 1);
+    off += __popcll(less & tb) << t;
+    total += __popcll(tb) << t;
   }
   const int sentinel = n;
   const int p = off * block_m + rank;
