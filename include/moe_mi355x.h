@@ -118,11 +118,12 @@ static inline int32_t moe_cap_tiles(int32_t tokens, int32_t topk, int32_t num_lo
 
 static inline size_t moe_align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-/* Workspace of moe_sort: per-chunk expert counts and per-row ranks (int32). */
+/* Workspace of moe_sort: per-chunk expert offsets plus each expert's first row and row count,
+ * and per-row ranks (int32). */
 static inline size_t moe_sort_ws_bytes(int32_t tokens, int32_t topk, int32_t num_local_experts) {
   int64_t n = (int64_t)tokens * topk;
   int64_t chunks = (n + MOE_SORT_CHUNK - 1) / MOE_SORT_CHUNK;
-  return moe_align256((size_t)chunks * (size_t)num_local_experts * 4) + moe_align256((size_t)n * 4);
+  return moe_align256((size_t)(chunks + 2) * (size_t)num_local_experts * 4) + moe_align256((size_t)n * 4);
 }
 
 /* Bytes of one intermediate row of inter_dim elements in dtype dt (codes only). */

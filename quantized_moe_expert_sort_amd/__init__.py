@@ -104,7 +104,7 @@ def sync_words(tokens, cap):
 def sort_ws_bytes(tokens, topk, num_local_experts):
     n = tokens * topk
     chunks = (n + SORT_CHUNK - 1) // SORT_CHUNK
-    return _align256(chunks * num_local_experts * 4) + _align256(n * 4)
+    return _align256((chunks + 2) * num_local_experts * 4) + _align256(n * 4)
 
 
 def row_bytes(cols, dt):

@@ -93,50 +93,70 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __r
     }
   }
   __syncthreads();
-  auto E = [&](int i) { return in_lds ? lds_e[i] : expert_ids[i]; };
-  const int per = (n + GROUP_THREADS - 1) / GROUP_THREADS;
-  const int t0 = threadIdx.x * per, t1 = min(n, t0 + per);
-  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  // the tile -> expert reads of the searches: one instantiation reads LDS, the other global
+  // memory (a select between the two would become a generic-address load on every step)
+  auto work = [&](auto E) {
+    const int per = (n + GROUP_THREADS - 1) / GROUP_THREADS;
+    const int t0 = threadIdx.x * per, t1 = min(n, t0 + per);
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 
-  // run bounds [rs, re) of tile t's expert; cached while consecutive tiles share the expert
-  int cur_e = INT32_MIN, rs = 0, re = 0;
-  auto bounds = [&](int t) {
-    const int e = E(t);
-    if (e == cur_e) return;
-    cur_e = e;
-    int lo = 0, hi = t;                      // first index with E >= e
-    while (lo < hi) { const int m = (lo + hi) >> 1; if (E(m) < e) lo = m + 1; else hi = m; }
-    rs = lo;
-    lo = t + 1; hi = n;                      // first index with E > e
-    while (lo < hi) { const int m = (lo + hi) >> 1; if (E(m) <= e) lo = m + 1; else hi = m; }
-    re = lo;
-  };
-  int starts = 0;
-  for (int t = t0; t < t1; ++t) {
-    bounds(t);
-    starts += ((t - rs) % group_size(re - rs)) == 0;
-  }
-  int scan = starts;
+    // run bounds [rs, re) of tile t's expert e = E(t), found by galloping outwards from t (steps
+    // 1, 2, 4, ...) and then bisecting the last step: a run of length r costs ~2 log2(r) reads,
+    // so the many one-tile experts of a skewed routing cost one read per bound
+    auto run_start = [&](int t, int e) {
+      int hi = t, lo = t - 1;                             // E(hi) == e
+      for (int d = 1; lo >= 0 && E(lo) == e; d <<= 1) { hi = lo; lo = hi - 2 * d; }
+      lo = max(lo, -1);                                   // lo == -1 or E(lo) != e
+      while (hi - lo > 1) { const int m = (lo + hi) >> 1; if (E(m) == e) hi = m; else lo = m; }
+      return hi;
+    };
+    auto run_end = [&](int t, int e) {
+      int lo = t, hi = t + 1;                             // E(lo) == e
+      for (int d = 1; hi < n && E(hi) == e; d <<= 1) { lo = hi; hi = lo + 2 * d; }
+      hi = min(hi, n);                                    // hi == n or E(hi) != e
+      while (hi - lo > 1) { const int m = (lo + hi) >> 1; if (E(m) == e) lo = m; else hi = m; }
+      return hi;
+    };
+    // cached while consecutive tiles share the expert; a new expert inside the chunk starts at t
+    int cur_e = INT32_MIN, rs = 0, re = 0;
+    auto bounds = [&](int t) {
+      const int e = E(t);
+      if (e == cur_e) return;
+      rs = cur_e == INT32_MIN ? run_start(t, e) : t;
+      cur_e = e;
+      re = run_end(t, e);
+    };
+    int starts = 0;
+    for (int t = t0; t < t1; ++t) {
+      bounds(t);
+      starts += ((t - rs) % group_size(re - rs)) == 0;
+    }
+    int scan = starts;
 #pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const int o = __shfl_up(scan, d, WAVE);
-    if (lane >= d) scan += o;
-  }
-  if (lane == WAVE - 1) tmp[w] = scan;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < GROUP_THREADS / WAVE; ++i) { const int c = tmp[i]; tmp[i] = run; run += c; }
-    tmp[GROUP_THREADS / WAVE] = run;
-  }
-  __syncthreads();
-  int gidx = tmp[w] + scan - starts;
-  cur_e = INT32_MIN;
-  for (int t = t0; t < t1; ++t) {
-    bounds(t);
-    const int gs = group_size(re - rs);
-    if ((t - rs) % gs == 0) groups[gidx++] = int2{t, min(gs, re - t)};
-  }
+    for (int d = 1; d < WAVE; d <<= 1) {
+      const int o = __shfl_up(scan, d, WAVE);
+      if (lane >= d) scan += o;
+    }
+    if (lane == WAVE - 1) tmp[w] = scan;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int run = 0;
+      for (int i = 0; i < GROUP_THREADS / WAVE; ++i) { const int c = tmp[i]; tmp[i] = run; run += c; }
+      tmp[GROUP_THREADS / WAVE] = run;
+    }
+    __syncthreads();
+    int gidx = tmp[w] + scan - starts;
+    cur_e = INT32_MIN;
+    for (int t = t0; t < t1; ++t) {
+      bounds(t);
+      const int gs = group_size(re - rs);
+      if ((t - rs) % gs == 0) groups[gidx++] = int2{t, min(gs, re - t)};
+    }
+  };
+  if (in_lds)
+    work([&](int i) { return lds_e[i]; });
+  else
+    work([&](int i) { return expert_ids[i]; });
   if (threadIdx.x == 0) *num_groups = tmp[GROUP_THREADS / WAVE];
 }
 

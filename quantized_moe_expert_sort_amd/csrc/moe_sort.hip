@@ -284,15 +284,19 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
 
 constexpr int SCAN_THREADS = 1024;
 
+// One workgroup: per expert, the chunk counts become exclusive offsets within the expert
+// (hist[c*E + e]); the expert's first row goes to first[e] and its row count to cnt[e]
+// (first = hist + nchunks*E, cnt = first + E), the tile total to num_tiles.  The layout itself
+// is written by the scatter's many workgroups (a single workgroup's scattered stores are bound
+// by its one CU's address unit).
 __global__ __launch_bounds__(SCAN_THREADS) void sort_scan_kernel(int* __restrict__ hist, int nchunks,
-                                                                 int E, int block_m, int sentinel,
-                                                                 SortLayout L) {
+                                                                 int E, int block_m, SortLayout L) {
   extern __shared__ int smem[];
   int* pos = smem;                       // [E]
   int* tmp = pos + E;                    // [SCAN_THREADS / WAVE + 1]
   // the counts of SB chunks are loaded together, then turned into exclusive offsets: a memory
   // latency per SB chunks instead of one per chunk
-  constexpr int SB = 16;
+  constexpr int SB = 32;
   for (int e = threadIdx.x; e < E; e += SCAN_THREADS) {
     int run = 0;
     for (int c0 = 0; c0 < nchunks; c0 += SB) {
@@ -308,37 +312,93 @@ __global__ __launch_bounds__(SCAN_THREADS) void sort_scan_kernel(int* __restrict
     pos[e] = run;
   }
   __syncthreads();
-  layout_from_counts<SCAN_THREADS>(pos, E, block_m, sentinel, L, tmp);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += SCAN_THREADS) {
-    const int first = pos[e];
-    for (int c0 = 0; c0 < nchunks; c0 += SB) {
-      int h[SB];
-#pragma unroll
-      for (int u = 0; u < SB; ++u) h[u] = c0 + u < nchunks ? hist[(int64_t)(c0 + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < SB; ++u)
-        if (c0 + u < nchunks) hist[(int64_t)(c0 + u) * E + e] = h[u] + first;
-    }
+  int* first = hist + (int64_t)nchunks * E;
+  int* cnt = first + E;
+  const int per = (E + SCAN_THREADS - 1) / SCAN_THREADS;
+  const int e0 = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (e0 + i < E) local += (pos[e0 + i] + block_m - 1) / block_m;
+  int total = 0;
+  int off = block_exclusive_scan<SCAN_THREADS>(local, tmp, &total);
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int c = pos[e];
+    first[e] = off * block_m;
+    cnt[e] = c;
+    off += (c + block_m - 1) / block_m;
   }
+  if (threadIdx.x == 0) *L.num_tiles = total;
 }
 
-__global__ __launch_bounds__(256) void sort_scatter_kernel(
+// Rows to their positions: SCATTER_SPLIT workgroups per chunk, each thread SCATTER_RPT rows with
+// all their loads issued together.  The row that opens a tile writes the tile's expert id, an
+// expert's last row writes the padding of its last tile, and all workgroups share the unused
+// tail (expert -1, sentinel rows).
+constexpr int SCATTER_THREADS = 256;
+constexpr int SCATTER_RPT = 4;
+constexpr int SCATTER_SPLIT = MOE_SORT_CHUNK / (SCATTER_THREADS * SCATTER_RPT);
+static_assert(SCATTER_SPLIT * SCATTER_THREADS * SCATTER_RPT == MOE_SORT_CHUNK, "whole chunks");
+
+__global__ __launch_bounds__(SCATTER_THREADS) void sort_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int64_t n, int expert_begin,
-    int E, const int* __restrict__ hist, const int* __restrict__ ranks, SortLayout L) {
-  const int64_t base = (int64_t)blockIdx.x * MOE_SORT_CHUNK;
-  for (int i = threadIdx.x; i < MOE_SORT_CHUNK; i += 256) {
-    const int64_t v = base + i;
-    if (v >= n) break;
-    const int k = ids[v] - expert_begin;
-    if (k < 0 || k >= E) {
+    int E, int block_m, int nchunks, const int* __restrict__ hist, const int* __restrict__ ranks,
+    SortLayout L) {
+  const int chunk = blockIdx.x / SCATTER_SPLIT;
+  const int64_t base = (int64_t)chunk * MOE_SORT_CHUNK +
+                       (int64_t)(blockIdx.x % SCATTER_SPLIT) * (SCATTER_THREADS * SCATTER_RPT);
+  const int* first = hist + (int64_t)nchunks * E;
+  const int* cnt = first + E;
+  const int sentinel = (int)n;
+  int k[SCATTER_RPT];
+#pragma unroll
+  for (int u = 0; u < SCATTER_RPT; ++u) {
+    const int64_t v = base + u * SCATTER_THREADS + threadIdx.x;
+    k[u] = v < n ? ids[v] - expert_begin : -1;
+  }
+  int f[SCATTER_RPT], h[SCATTER_RPT], r[SCATTER_RPT], c[SCATTER_RPT];
+  float w[SCATTER_RPT];
+#pragma unroll
+  for (int u = 0; u < SCATTER_RPT; ++u) {
+    const int64_t v = base + u * SCATTER_THREADS + threadIdx.x;
+    const bool ok = k[u] >= 0 && k[u] < E;
+    const int kk = ok ? k[u] : 0;
+    f[u] = first[kk];
+    c[u] = cnt[kk];
+    h[u] = hist[(int64_t)chunk * E + kk];
+    r[u] = ok ? ranks[v] : 0;
+    w[u] = ok && L.sorted_w ? topk_w[v] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < SCATTER_RPT; ++u) {
+    const int64_t v = base + u * SCATTER_THREADS + threadIdx.x;
+    if (v >= n) continue;
+    if (k[u] < 0 || k[u] >= E) {
       if (L.row_of) L.row_of[v] = -1;
       continue;
     }
-    const int p = hist[(int64_t)blockIdx.x * E + k] + ranks[v];
+    const int q = h[u] + r[u];                            // rank within the expert
+    const int p = f[u] + q;
     L.sorted_ids[p] = (int32_t)v;
-    if (L.sorted_w) L.sorted_w[p] = topk_w[v];
+    if (L.sorted_w) L.sorted_w[p] = w[u];
     if (L.row_of) L.row_of[v] = p;
+    if ((q & (block_m - 1)) == 0) L.expert_ids[p / block_m] = k[u];   // f is a multiple of block_m
+    if (q == c[u] - 1) {
+      const int end = f[u] + (c[u] + block_m - 1) / block_m * block_m;
+      for (int pp = p + 1; pp < end; ++pp) {
+        L.sorted_ids[pp] = sentinel;
+        if (L.sorted_w) L.sorted_w[pp] = 0.0f;
+      }
+    }
+  }
+  const int64_t total = *L.num_tiles;
+  const int64_t tid = (int64_t)blockIdx.x * SCATTER_THREADS + threadIdx.x;
+  const int64_t nth = (int64_t)gridDim.x * SCATTER_THREADS;
+  for (int64_t t = total + tid; t < L.cap_tiles; t += nth) L.expert_ids[t] = -1;
+  for (int64_t pp = total * block_m + tid; pp < (int64_t)L.cap_tiles * block_m; pp += nth) {
+    L.sorted_ids[pp] = sentinel;
+    if (L.sorted_w) L.sorted_w[pp] = 0.0f;
   }
 }
 
@@ -359,16 +419,17 @@ hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, 
   }
   const int nchunks = (int)((n + MOE_SORT_CHUNK - 1) / MOE_SORT_CHUNK);
   int* hist = (int*)ws;
-  int* ranks = (int*)((char*)ws + moe_align256((size_t)nchunks * E * sizeof(int)));
+  int* ranks = (int*)((char*)ws + moe_align256((size_t)(nchunks + 2) * E * sizeof(int)));
   sort_count_kernel<<<nchunks, SORT_THREADS, (size_t)E * sizeof(int) + wc_bytes, s>>>(
       topk_ids, n, expert_begin, E, hist, ranks, L);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scan_kernel<<<1, SCAN_THREADS, (size_t)(E + SCAN_THREADS / WAVE + 1) * sizeof(int), s>>>(
-      hist, nchunks, E, block_m, sentinel, L);
+      hist, nchunks, E, block_m, L);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  sort_scatter_kernel<<<nchunks, 256, 0, s>>>(topk_ids, topk_w, n, expert_begin, E, hist, ranks, L);
+  sort_scatter_kernel<<<nchunks * SCATTER_SPLIT, SCATTER_THREADS, 0, s>>>(topk_ids, topk_w, n, expert_begin, E,
+                                                                        block_m, nchunks, hist, ranks, L);
   return hipGetLastError();
 }
 
