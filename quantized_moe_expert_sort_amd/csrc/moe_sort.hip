@@ -127,41 +127,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return res;
 }
 
-// Per-expert row counts -> tile offsets, expert_ids, padding sentinels, tail, num_tiles.
-// counts[e] holds c_e on entry and the first row position of expert e on exit.
-template <int NT>
-__device__ void layout_from_counts(int* counts, int E, int block_m, int sentinel,
-                                   const SortLayout& L, int* tmp) {
-  const int per = (E + NT - 1) / NT;
-  const int e0 = threadIdx.x * per;
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int e = e0 + i;
-    if (e < E) local += (counts[e] + block_m - 1) / block_m;
-  }
-  int total = 0;
-  int off = block_exclusive_scan<NT>(local, tmp, &total);
-  for (int i = 0; i < per; ++i) {
-    const int e = e0 + i;
-    if (e >= E) break;
-    const int c = counts[e];
-    const int nt = (c + block_m - 1) / block_m;
-    for (int t = 0; t < nt; ++t) L.expert_ids[off + t] = e;
-    const int64_t first = (int64_t)off * block_m;
-    for (int p = c; p < nt * block_m; ++p) {          // padding of this expert's last tile
-      L.sorted_ids[first + p] = sentinel;
-      if (L.sorted_w) L.sorted_w[first + p] = 0.0f;
-    }
-    counts[e] = (int)first;
-    off += nt;
-  }
-  for (int64_t t = total + threadIdx.x; t < L.cap_tiles; t += NT) L.expert_ids[t] = -1;
-  for (int64_t p = (int64_t)total * block_m + threadIdx.x; p < (int64_t)L.cap_tiles * block_m; p += NT) {
-    L.sorted_ids[p] = sentinel;
-    if (L.sorted_w) L.sorted_w[p] = 0.0f;
-  }
-  if (threadIdx.x == 0) *L.num_tiles = total;
-}
 
 // The layout's sync words (a multiple of 4, 16-byte aligned) set to zero by threads
 // first, first + stride, ...
@@ -233,32 +198,77 @@ __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restri
   if (lane == 0) *L.num_tiles = total;
 }
 
-// ---------------------------------------------------------------- one-workgroup path
+// ---------------------------------------------------------------- one-chunk path
+//
+// Rows <= MOE_SORT_CHUNK: SMALL_SORT_WGS workgroups each rank every row and scan the experts
+// (the input is at most 16 KB), then write a share of the layout: workgroup g the rows of round
+// g of every wave (with the tile expert ids from each tile's first row and the padding from
+// each expert's last row) and a slice of the unused tail.  One workgroup writing everything
+// was bound by its CU's address unit.
+
+constexpr int SMALL_SORT_WGS = ROUNDS;
 
 __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int n, int expert_begin,
     int E, int block_m, SortLayout L) {
   extern __shared__ int smem[];
-  int* pos = smem;                                             // [E]
-  int* tmp = pos + E;                                          // [SORT_WAVES + 1]
+  int* cnt = smem;                                             // [E] rows per expert
+  int* tmp = cnt + E;                                          // [SORT_WAVES + 1]
   uint16_t* wc = reinterpret_cast<uint16_t*>(tmp + SORT_WAVES + 1);   // [SORT_WAVES][E]
   int key[ROUNDS], rank[ROUNDS];
-  rank_chunk(ids, 0, n, expert_begin, E, wc, pos, key, rank);
-  zero_sync(L, threadIdx.x, SORT_THREADS);
-  layout_from_counts<SORT_THREADS>(pos, E, block_m, n, L, tmp);
+  rank_chunk(ids, 0, n, expert_begin, E, wc, cnt, key, rank);
+  zero_sync(L, (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x, (int64_t)gridDim.x * SORT_THREADS);
+  // first row of every expert (into the consumed per-wave counters; the scan's barriers order
+  // these writes after every counter read)
+  int* first = reinterpret_cast<int*>(wc);
+  const int per = (E + SORT_THREADS - 1) / SORT_THREADS;
+  const int e0 = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (e0 + i < E) local += (cnt[e0 + i] + block_m - 1) / block_m;
+  int total = 0;
+  int off = block_exclusive_scan<SORT_THREADS>(local, tmp, &total);
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    first[e] = off * block_m;
+    off += (cnt[e] + block_m - 1) / block_m;
+  }
   __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x == 0) *L.num_tiles = total;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  const int sentinel = n;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
+    if (r % (int)gridDim.x != (int)blockIdx.x) continue;
     const int v = w * SUB + r * WAVE + lane;
-    if (key[r] < 0) {
-      if (L.row_of && v < n) L.row_of[v] = -1;
+    if (v >= n) continue;
+    const int k = key[r];
+    if (k < 0) {
+      if (L.row_of) L.row_of[v] = -1;
       continue;
     }
-    const int p = pos[key[r]] + rank[r];
+    const int q = rank[r];                                     // rank within the expert
+    const int f = first[k], p = f + q;
     L.sorted_ids[p] = v;
     if (L.sorted_w) L.sorted_w[p] = topk_w[v];
     if (L.row_of) L.row_of[v] = p;
+    if ((q & (block_m - 1)) == 0) L.expert_ids[p / block_m] = k;   // f is a multiple of block_m
+    const int c = cnt[k];
+    if (q == c - 1) {
+      const int end = f + (c + block_m - 1) / block_m * block_m;
+      for (int pp = p + 1; pp < end; ++pp) {
+        L.sorted_ids[pp] = sentinel;
+        if (L.sorted_w) L.sorted_w[pp] = 0.0f;
+      }
+    }
+  }
+  const int64_t tid = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
+  const int64_t nth = (int64_t)gridDim.x * SORT_THREADS;
+  for (int64_t t = total + tid; t < L.cap_tiles; t += nth) L.expert_ids[t] = -1;
+  for (int64_t pp = (int64_t)total * block_m + tid; pp < (int64_t)L.cap_tiles * block_m; pp += nth) {
+    L.sorted_ids[pp] = sentinel;
+    if (L.sorted_w) L.sorted_w[pp] = 0.0f;
   }
 }
 
@@ -414,7 +424,8 @@ hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, 
   }
   if (n <= MOE_SORT_CHUNK) {
     const size_t lds = (size_t)(E + SORT_WAVES + 1) * sizeof(int) + wc_bytes;
-    sort_small_kernel<<<1, SORT_THREADS, lds, s>>>(topk_ids, topk_w, (int)n, expert_begin, E, block_m, L);
+    sort_small_kernel<<<SMALL_SORT_WGS, SORT_THREADS, lds, s>>>(topk_ids, topk_w, (int)n, expert_begin, E,
+                                                              block_m, L);
     return hipGetLastError();
   }
   const int nchunks = (int)((n + MOE_SORT_CHUNK - 1) / MOE_SORT_CHUNK);
