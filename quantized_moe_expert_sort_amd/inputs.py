@@ -62,6 +62,9 @@ WORKLOADS = {
     "mid-1024": Workload("mid-1024", 1024, 896, 16, 3584, 384, "fp8"),
     "ep-8192": Workload("ep-8192", 8192, 112, 16, 3584, 3072, "fp8", global_experts=896),
     "pre-16384": Workload("pre-16384", 16384, 896, 16, 3584, 384, "fp4", zipf_s=1.1),
+    # the pages' own large-batch timing shape (uniform routing over all 896 experts)
+    "pre-a16-8192": Workload("pre-a16-8192", 8192, 896, 16, 3584, 384, "bf16"),
+    "pre-a8-8192": Workload("pre-a8-8192", 8192, 896, 16, 3584, 384, "fp8"),
 }
 
 # ----------------------------------------------------------------------------- generators

@@ -138,7 +138,8 @@ def weights_for(wl):
     return _WEIGHTS[key]
 
 
-FULL = ["dec-1", "dec-4", "dec-16", "mid-64", "mid-256", "mid-1024", "pre-16384", "ep-8192"]
+FULL = ["dec-1", "dec-4", "dec-16", "mid-64", "mid-256", "mid-1024", "pre-16384", "ep-8192", "pre-a16-8192",
+        "pre-a8-8192"]
 
 
 @pytest.mark.parametrize("name", FULL)
