@@ -131,11 +131,11 @@ static inline size_t moe_row_bytes(int32_t cols, int32_t dt) {
   return dt == MOE_DT_BF16 ? (size_t)cols * 2 : dt == MOE_DT_FP8_E4M3 ? (size_t)cols : (size_t)cols / 2;
 }
 
-/* Bytes per element of the per-row Stage2 outputs: fp32 for bf16 activations, bf16 otherwise. */
-static inline size_t moe_rowout_elem_bytes(int32_t a_dtype) { return a_dtype == MOE_DT_BF16 ? 4 : 2; }
+/* Bytes per element of the per-row Stage2 outputs (bf16 for every activation dtype). */
+static inline size_t moe_rowout_elem_bytes(int32_t a_dtype) { (void)a_dtype; return 2; }
 
 /* Workspace of moe_fused, in this order (each part 256-byte aligned): the per-row Stage2 outputs
- * [cap*bm, D] (router weight applied; fp32 or bf16, see moe_rowout_elem_bytes), the stage1
+ * [cap*bm, D] (bf16; router weight applied on the per-tile path, see moe_rowout_elem_bytes), the stage1
  * intermediate [cap*bm, I] in a_dtype plus its [cap*bm, I/32] e8m0 scales (fp8/fp4), a
  * [cap] list of tile groups plus its count (large batches), and for NONE_TEST a fp32
  * [cap*bm, 2I] debug area holding the raw gate (cols 0..I-1) and up (I..2I-1) sums of each

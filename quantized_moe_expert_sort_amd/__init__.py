@@ -112,7 +112,7 @@ def row_bytes(cols, dt):
 
 
 def rowout_elem_bytes(a_dtype):
-    return 4 if a_dtype == DT_BF16 else 2
+    return 2
 
 
 def fused_debug_offset(tokens, model_dim, inter_dim, cap, block_m, a_dtype):

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(THREADS, MINW) void stage2_kernel(FusedArgs p, int 
 // W: the rows were stored without the router weight (grouped Stage2); each is multiplied by
 // topk_w[t*topk + k] in fp32 before it is added.
 
-template <bool F32, bool W = false>
+template <bool W = false>
 __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restrict__ rowout,
                                                           const int32_t* __restrict__ row_of,
                                                           uint16_t* __restrict__ out, int T, int topk,
@@ -67,44 +67,25 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
     int r[KG];
 #pragma unroll
     for (int u = 0; u < KG; ++u) r[u] = k0 + u < topk ? row_of[(int64_t)t * topk + k0 + u] : -1;
-    if (F32) {
-      float4 a[KG], b[KG];
+    uint4 q[KG];
+    float wk[KG];
 #pragma unroll
-      for (int u = 0; u < KG; ++u) {
-        if (r[u] >= 0) {
-          const float4* src = reinterpret_cast<const float4*>(rowout + ((size_t)r[u] * D + c) * 4);
-          a[u] = src[0];
-          b[u] = src[1];
+    for (int u = 0; u < KG; ++u) {
+      q[u] = r[u] >= 0 ? *reinterpret_cast<const uint4*>(rowout + ((size_t)r[u] * D + c) * 2)
+                       : uint4{0u, 0u, 0u, 0u};
+      if (W) wk[u] = r[u] >= 0 ? topk_w[(int64_t)t * topk + k0 + u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+      const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (W) {
+          sum[2 * h] += wk[u] * __uint_as_float(w[h] << 16);
+          sum[2 * h + 1] += wk[u] * __uint_as_float(w[h] & 0xFFFF0000u);
         } else {
-          a[u] = b[u] = float4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < KG; ++u) {
-        sum[0] += a[u].x; sum[1] += a[u].y; sum[2] += a[u].z; sum[3] += a[u].w;
-        sum[4] += b[u].x; sum[5] += b[u].y; sum[6] += b[u].z; sum[7] += b[u].w;
-      }
-    } else {
-      uint4 q[KG];
-      float wk[KG];
-#pragma unroll
-      for (int u = 0; u < KG; ++u) {
-        q[u] = r[u] >= 0 ? *reinterpret_cast<const uint4*>(rowout + ((size_t)r[u] * D + c) * 2)
-                         : uint4{0u, 0u, 0u, 0u};
-        if (W) wk[u] = r[u] >= 0 ? topk_w[(int64_t)t * topk + k0 + u] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < KG; ++u) {
-        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          if (W) {
-            sum[2 * h] += wk[u] * __uint_as_float(w[h] << 16);
-            sum[2 * h + 1] += wk[u] * __uint_as_float(w[h] & 0xFFFF0000u);
-          } else {
-            sum[2 * h] += __uint_as_float(w[h] << 16);
-            sum[2 * h + 1] += __uint_as_float(w[h] & 0xFFFF0000u);
-          }
+          sum[2 * h] += __uint_as_float(w[h] << 16);
+          sum[2 * h + 1] += __uint_as_float(w[h] & 0xFFFF0000u);
         }
       }
     }
@@ -126,8 +107,8 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
 // tiles past num_tiles carry expert -1, so num_tiles itself is never waited for); for each
 // tile a wave computes the 16 x 16 block (tile rows x the block's
 // columns) with exactly the MFMA sequence of stage2_item (same operands, K steps ascending),
-// scales it by the router weight and rounds it as stage2_item stores it (fp32 for bf16
-// activations, bf16 otherwise) into slot [t*topk + k] of an LDS array.  The token sums then run
+// scales it by the router weight and rounds it to bf16 as stage2_item stores it, into slot
+// [t*topk + k] of an LDS array.  The token sums then run
 // over k ascending with 0 for non-local rows, as the combine kernel does: the output has the
 // same bits as Stage2 + combine, without the per-row buffer or the extra launch.
 
@@ -244,7 +225,7 @@ __global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p
         const int v = vrow[f][i];
         if ((unsigned)v < (unsigned)TK) {
           const float o = acc[f][i] * wv[f][i];
-          vals[v][r16] = ADT == DT_BF16 ? o : __uint_as_float((uint32_t)f32_to_bf16_rne(o) << 16);
+          vals[v][r16] = __uint_as_float((uint32_t)f32_to_bf16_rne(o) << 16);
         }
       }
   }
@@ -325,10 +306,8 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
   }
   const int64_t nthreads = (int64_t)a.T * (a.D / 8);
   const unsigned gridc = (unsigned)((nthreads + THREADS - 1) / THREADS);
-  if (ADT == DT_BF16)
-    combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
-  else if (tiled2)   // grouped Stage2 rows carry no router weight
-    combine_kernel<false, true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, a.topk_w);
+  if (tiled2)   // grouped Stage2 rows carry no router weight
+    combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, a.topk_w);
   else
     combine_kernel<false><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
   return hipGetLastError();

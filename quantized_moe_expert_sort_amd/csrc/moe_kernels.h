@@ -39,7 +39,7 @@ struct FusedArgs {
   const int32_t* expert_ids;
   const int32_t* num_tiles;
   const int32_t* row_of;   // [T*topk] position of each routed row or -1
-  uint8_t* rowout;         // [cap*bm, D] weighted stage2 rows (fp32 for bf16 activations, else bf16)
+  uint8_t* rowout;         // [cap*bm, D] stage2 rows (bf16)
   uint8_t* inter;          // [cap*bm, I] intermediate codes
   uint8_t* inter_s;        // [cap*bm, I/32] intermediate scales (fp8 / fp4)
   int2* groups;            // [cap] tile groups (large-batch path)

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(THREADS, 2) void single_kernel(FusedArgs p, int n1,
   for (int i = 0; i < nt; ++i) {
     const int t = todo[i];
     for (int blk = cls; blk < n2; blk += MOE_SYNC_CLASSES)
-      combine_token_cols<ADT == DT_BF16, true>(p, t, blk * C::NO, min((blk + 1) * C::NO, p.D));
+      combine_token_cols<true>(p, t, blk * C::NO, min((blk + 1) * C::NO, p.D));
   }
 }
 

@@ -14,9 +14,9 @@
 //   one e8m0 scale per 32 columns (the 32 columns of a block are 32 lanes of one wave).
 // Stage2 item (tile, nb) (PR 5118 review items 9-10: bf16 x MXFP4 stage2 with a per-token
 //   scatter of the weighted rows): block_m rows x 64*NF output columns (the last block of a row
-//   may be partial); each wave owns 16*NF columns over the whole K = inter_dim.  The fp32 result row is scaled by the router weight
-//   of its routed row and stored as that routed row's output (fp32 for bf16 activations, bf16
-//   otherwise).
+//   may be partial); each wave owns 16*NF columns over the whole K = inter_dim.  The fp32 result
+//   row is scaled by the router weight of its routed row and stored, rounded to bf16, as that
+//   routed row's output.
 // Combine: each token's routed-row outputs summed in ascending k in fp32, rounded to bf16.
 #pragma once
 
@@ -546,14 +546,10 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
 #pragma unroll
       for (int j = 0; j < NF; ++j) {
         const float o = acc[f][j][i] * wrow[f][i];
-        if (ADT == DT_BF16) {
-          if (valid) st<COH>(reinterpret_cast<float*>(p.rowout) + R * D + c0 + 16 * j, o);
-        } else {
-          const uint32_t h = f32_to_bf16_rne(o);
-          const uint32_t h1 = (uint32_t)__shfl_down((int)h, 1, WAVE);
-          if (valid && (r16 & 1) == 0)
-            st<COH>(reinterpret_cast<uint32_t*>(p.rowout + (R * D + c0 + 16 * j) * 2), h | (h1 << 16));
-        }
+        const uint32_t h = f32_to_bf16_rne(o);
+        const uint32_t h1 = (uint32_t)__shfl_down((int)h, 1, WAVE);
+        if (valid && (r16 & 1) == 0)
+          st<COH>(reinterpret_cast<uint32_t*>(p.rowout + (R * D + c0 + 16 * j) * 2), h | (h1 << 16));
       }
     }
   }
@@ -573,19 +569,15 @@ __device__ __forceinline__ void token_rows(const FusedArgs& p, int t, int k0, in
 }
 
 // Two neighbouring columns c, c+1 of routed row r (0 where r < 0).
-template <bool F32, bool COH>
+template <bool COH>
 __device__ __forceinline__ float2 rowout_pair(const FusedArgs& p, int r, int c) {
   if (r < 0) return float2{0.f, 0.f};
-  if (F32) {
-    const uint64_t q = ld<COH>(reinterpret_cast<const uint64_t*>(p.rowout + ((size_t)r * p.D + c) * 4));
-    return float2{__uint_as_float((uint32_t)q), __uint_as_float((uint32_t)(q >> 32))};
-  }
   const uint32_t q = ld<COH>(reinterpret_cast<const uint32_t*>(p.rowout + ((size_t)r * p.D + c) * 2));
   return float2{__uint_as_float(q << 16), __uint_as_float(q & 0xFFFF0000u)};
 }
 
 // Columns [c_begin, c_end) of token t, two per thread of the workgroup.
-template <bool F32, bool COH>
+template <bool COH>
 __device__ __forceinline__ void combine_token_cols(const FusedArgs& p, int t, int c_begin, int c_end) {
   constexpr int KG = 8;
   for (int c = c_begin + 2 * (int)threadIdx.x; c < c_end; c += 2 * (int)blockDim.x) {
@@ -595,7 +587,7 @@ __device__ __forceinline__ void combine_token_cols(const FusedArgs& p, int t, in
       token_rows<KG>(p, t, k0, r);
       float2 v[KG];
 #pragma unroll
-      for (int u = 0; u < KG; ++u) v[u] = rowout_pair<F32, COH>(p, r[u], c);
+      for (int u = 0; u < KG; ++u) v[u] = rowout_pair<COH>(p, r[u], c);
 #pragma unroll
       for (int u = 0; u < KG; ++u) { s0 += v[u].x; s1 += v[u].y; }
     }
