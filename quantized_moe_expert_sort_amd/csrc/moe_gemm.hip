@@ -241,11 +241,13 @@ __global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p
 // Stage tiling per activation dtype and block_m.
 template <int ADT, int BM>
 struct Cfg {
-  // intermediate columns / workgroup: 64 at 32-row fp8/fp4 tiles halves the re-reads of the
-  // gathered activation rows (measured 3% faster at 1024 tokens; slower at 16-row tiles)
-  static constexpr int NI = ADT == DT_BF16 ? 16 : (BM == 32 ? 64 : 32);
+  // intermediate columns / workgroup: wider at 32-row tiles, where the re-reads of the gathered
+  // activation rows by the workgroups of one tile dominate (fp8/fp4: 64, 3% faster at 1024
+  // tokens; bf16: 32, Stage1 30% faster at 8192 tokens); slower at 16-row tiles
+  static constexpr int NI = BM == 32 ? (ADT == DT_BF16 ? 32 : 64) : (ADT == DT_BF16 ? 16 : 32);
   static constexpr int KW = 4;                                // waves splitting K in stage1
-  static constexpr int PF1 = BM == 16 ? 7 : (NI == 64 ? 2 : 4);   // K steps in flight per wave
+  // K steps in flight per wave (the bf16 operands are 4x the fp4 ones in registers)
+  static constexpr int PF1 = BM == 16 ? 7 : (ADT == DT_BF16 || NI == 64 ? 2 : 4);
   static constexpr int MINW1 = 2;                               // waves per SIMD kept
   // activation rows staged in LDS (fp8 measured faster with its rows in registers)
   static constexpr bool LDSA = BM == 16 && ADT != DT_FP8;
