@@ -208,7 +208,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // row % 16, so the fragments of a wave differ by constant offsets.
 template <int CPR>
 __device__ __forceinline__ int swz_slot(int row, int part) {
-  if constexpr (CPR == 8) return row * 8 + (part ^ (((row >> 1) ^ (row << 2)) & 7));
+  if constexpr (CPR == 16) return row * 16 + (part ^ (row & 15));
+  else if constexpr (CPR == 8) return row * 8 + (part ^ (((row >> 1) ^ (row << 2)) & 7));
   else return row * 4 + (part ^ ((row ^ (row >> 2)) & 3));
 }
 
@@ -224,19 +225,25 @@ __device__ __forceinline__ int swz_slot(int row, int part) {
 
 constexpr int NLOAD = 4;                      // loader waves
 
+// bf16 activations (Stage1 only): an item takes one half of a group (up to 4 tiles, 128 rows),
+// so the 256-byte A row pieces of a K step leave room for three buffers; the B side (fp4 rows,
+// scale chunks) is that of fp8 / fp4.
 template <int ADT>
 struct GFmt {
-  static constexpr int KA = ADT == DT_FP8 ? 128 : 64;     // A bytes per row per K step
+  static constexpr int GTA = ADT == DT_BF16 ? GT / 2 : GT;   // sort tiles per item, at most
+  static constexpr int BM = GTA * 32;                     // rows per group
+  static constexpr int MF = BM / WM / 16;                 // 16-row A fragments per wave
+  static constexpr int KA = ADT == DT_FP8 ? 128 : ADT == DT_FP4 ? 64 : 256;   // A bytes per row per K step
   static constexpr int ACPR = KA / 16;                    // 16-byte chunks per A row
-  static constexpr int P = ADT == DT_FP8 ? 3 : 4;         // LDS buffers = K steps in flight + 1
-  static constexpr int AD = ADT == DT_FP8 ? 2 : 3;        // A fragments read ahead of the MFMAs
-  static constexpr int A_BYTES = BMW * KA;
+  static constexpr int P = ADT == DT_FP4 ? 4 : 3;         // LDS buffers = K steps in flight + 1
+  static constexpr int AD = ADT == DT_FP8 ? 2 : ADT == DT_FP4 ? 3 : 1;   // A fragments read ahead of the MFMAs
+  static constexpr int A_BYTES = BM * KA;
   static constexpr int B_BYTES = BNW * 64;
   static constexpr int BUF = A_BYTES + B_BYTES + (BMW + BNW) * 4;
   static constexpr int A_IPL = A_BYTES / 1024 / NLOAD;    // A copy instructions per loader per step
   static constexpr int B_IPL = B_BYTES / 1024 / NLOAD;
   static constexpr int ROWS_PER_AI = 1024 / KA;           // A rows covered by one instruction
-  static constexpr int OB = ADT == DT_FP8 ? BNW / 2 : BNW / 4;   // Stage1 output code bytes per row
+  static constexpr int OB = ADT == DT_FP8 ? BNW / 2 : ADT == DT_FP4 ? BNW / 4 : BNW;   // Stage1 output bytes per row
   static constexpr int OBS = OB + 16;                     // their LDS row stride
 };
 
@@ -245,13 +252,15 @@ struct GFmt {
 // row's scales arrive with one 16-byte copy per four steps instead of a 4-byte copy per step
 // (a copy instruction whose 64 lanes touch 64 different cache lines costs the memory pipeline
 // as much as one that moves a kilobyte).  fp4 activations take A and B scales in chunks; the
-// fp8 A tile leaves room for the B chunks only.
+// fp8 A tile leaves room for the B chunks only (its A scale dwords travel with each step); bf16
+// activations have no scales.
 template <int ADT>
 struct S1Fmt {
   using F = GFmt<ADT>;
   static constexpr bool AW = ADT == DT_FP4;               // A scales in chunks
-  static constexpr int BUF = F::A_BYTES + F::B_BYTES + (AW ? 0 : BMW * 4);
-  static constexpr int A_SLOT = AW ? BMW * 16 : 0;
+  static constexpr bool AS1 = ADT == DT_FP8;              // A scale dwords per step
+  static constexpr int BUF = F::A_BYTES + F::B_BYTES + (AS1 ? F::BM * 4 : 0);
+  static constexpr int A_SLOT = AW ? F::BM * 16 : 0;
   static constexpr int SLOT = A_SLOT + BNW * 16;
   static constexpr int BYTES = F::P * BUF + 2 * SLOT;
 };
@@ -262,15 +271,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
                                                                     int n_nblk) {
   using F = GFmt<ADT>;
   using L1 = S1Fmt<ADT>;
-  constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P;
-  constexpr bool AW = L1::AW;
+  constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P, BM = F::BM, MF = F::MF;
+  constexpr bool AW = L1::AW, AS1 = L1::AS1, HAS_AS = AW || AS1;
   static_assert(F::A_IPL * NLOAD * 1024 == F::A_BYTES && F::B_IPL * NLOAD * 1024 == F::B_BYTES, "copy split");
-  static_assert(BMW == NLOAD * WAVE && BNW == NLOAD * WAVE, "one scale copy of each operand per loader");
-  static_assert(BMW * (F::OBS + 4) <= P * L1::BUF, "staging fits");
+  static_assert((!HAS_AS || BM == NLOAD * WAVE) && BNW == NLOAD * WAVE, "one scale copy of each operand per loader");
+  static_assert(BM * (F::OBS + 4) <= P * L1::BUF, "staging fits");
   static_assert(P <= 5, "a chunk slot is refilled only after the four steps of its previous chunk");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L1::BYTES];
-  __shared__ int lds_v[BMW];
+  __shared__ int lds_v[BM];
 
   const int TK = p.T * p.topk, D = p.D, I = p.I;
   const int lane = threadIdx.x & (WAVE - 1);
@@ -284,20 +293,33 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
   const uint32_t lds0 = lds_addr(lds);
   const uint32_t slot0 = lds0 + P * L1::BUF;
 
-  // groups gi = xcd, xcd + 8, ... run on XCD xcd; item (group, column block)
+  // groups gi = xcd, xcd + 8, ... run on XCD xcd; item (group, part, column block), where a
+  // bf16 group is taken in two parts of at most GTA tiles.  The items of one group are
+  // consecutive, so they run at the same time on CUs of one XCD and fetch the group's
+  // activation rows and weight rows into its L2 once.
+  constexpr int PARTS = GT / F::GTA;
   const int ng = *num_groups;
   const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
-  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_nblk;
+  const int per_group = PARTS * n_nblk;
+  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * per_group;
 
   for (int local = local0; local < items_here; local += stride) {
-    const int gl = local / n_nblk, nb = local - gl * n_nblk;
+    const int gl = local / per_group, rem = local - gl * per_group;
+    const int part = rem / n_nblk, nb = rem - part * n_nblk;
     const int gi = gl * 8 + xcd;
     const int2 grp = groups[gi];
-    const int tile0 = grp.x, rows_used = grp.y * 32;
+    int tile0 = grp.x, ntile = grp.y;
+    if (PARTS == 2) {                                     // parts of ceil(n/2) and floor(n/2) tiles
+      const int h0 = (grp.y + 1) >> 1;
+      tile0 += part ? h0 : 0;
+      ntile = part ? grp.y - h0 : h0;
+    }
+    if (ntile == 0) continue;                             // a one-tile group's empty part
+    const int rows_used = ntile * 32;
     const int e = p.expert_ids[tile0];
     const int row_base = tile0 * 32;                      // first layout row of the group
-    if (loader) {
-      const int r = threadIdx.x;                          // < BMW
+    if (threadIdx.x < BM) {                               // loader lanes
+      const int r = threadIdx.x;
       lds_v[r] = r < rows_used ? p.sorted_ids[row_base + r] : TK;
     }
     lds_barrier();
@@ -339,11 +361,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
     }
     // scales: loader lw copies those of A rows and of B rows [64 lw, 64 lw + 64)
     const int sc_row = lw * WAVE + lane;
-    const bool as_on = lw * WAVE < rows_used;
-    const uint32_t as_off = a_src_index(sc_row) * (uint32_t)(K / 32);
+    const bool as_on = HAS_AS && lw * WAVE < rows_used;
+    const uint32_t as_off = HAS_AS ? a_src_index(sc_row) * (uint32_t)(K / 32) : 0u;
     const uint32_t bs_off = (uint32_t)b_row(sc_row) * (uint32_t)(K / 32);
     // copy instructions a loader issues for step s: the chunks travel with steps 0, 4, 8, ...
-    const int n_data = n_ai + F::B_IPL + (!AW && as_on ? 1 : 0);
+    const int n_data = n_ai + F::B_IPL + (AS1 && as_on ? 1 : 0);
     const int n_chunk = 1 + (AW && as_on ? 1 : 0);
 
     // per step the K advance goes into the (scalar) global base; lane offsets stay fixed.  The
@@ -364,15 +386,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 #pragma unroll
       for (int i = 0; i < F::B_IPL; ++i)
         dma16(bb, b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
-      if (!AW && as_on) dma4(as_base + s * 4, as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
+      if (AS1 && as_on) dma4(as_base + s * 4, as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
     };
 
     // the wave's B fragment rows: gate rows [32wn, 32wn+32) and the same up rows
     auto b_frag_row = [&](int j) -> int { return j < 2 ? 32 * wn + 16 * j : BNW / 2 + 32 * wn + 16 * (j - 2); };
-    const int arow0 = 128 * wm;                           // the wave's first A row
+    const int arow0 = (BM / WM) * wm;                     // the wave's first A row
     // A fragments of this wave that hold group rows: rows_used is a multiple of 32, so 0, 2, 4,
-    // 6 or 8; the MFMA loop is instantiated per count (no per-fragment branches inside it)
-    const int n_af = max(0, min(MFW, (rows_used - arow0) / 16));
+    // 6 or 8 (bf16: 0, 2 or 4); the MFMA loop is instantiated per count (no per-fragment
+    // branches inside it)
+    const int n_af = max(0, min(MF, (rows_used - arow0) / 16));
 
     auto run = [&](auto na_c) {
       constexpr int NA = decltype(na_c)::value;
@@ -382,7 +405,52 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 #pragma unroll
         for (int j = 0; j < NFW; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-      auto compute = [&](int s) {
+      auto compute_bf16 = [&](int s) {
+        const uint8_t* la = lds + (s % P) * L1::BUF;
+        const uint8_t* lb = la + F::A_BYTES;
+        const uint8_t* slot = lds + P * L1::BUF + ((s >> 2) & 1) * L1::SLOT;
+        const int kq = (s & 3) * 4;
+        // lane group g takes K [32 g, 32 g + 32) of the step (one scale block) for both
+        // operands: four 32-deep bf16 MFMAs, sub-step jj on K [32 g + 8 jj, 32 g + 8 jj + 8);
+        // the fp4 weights are widened to bf16 once per step with the scaled converts
+        v8bf bop[NFW][4];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          const int br = b_frag_row(j) + r16;
+          const uint4 q = *reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16);
+          const uint32_t bs = (*reinterpret_cast<const uint32_t*>(slot + L1::A_SLOT + br * 16 + kq) >> (8 * g)) & 0xFFu;
+          const float sc = e8m0_to_float(bs);
+          bop[j][0] = fp4x8_to_bf16(q.x, sc);
+          bop[j][1] = fp4x8_to_bf16(q.y, sc);
+          bop[j][2] = fp4x8_to_bf16(q.z, sc);
+          bop[j][3] = fp4x8_to_bf16(q.w, sc);
+        }
+        auto load_a = [&](int f, v8bf* a) {
+          const int ar = arow0 + 16 * f + r16;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint4 q = *reinterpret_cast<const uint4*>(la + swz_slot<16>(ar, 4 * g + jj) * 16);
+            a[jj] = as_bf16x8(q.x, q.y, q.z, q.w);
+          }
+        };
+        constexpr int AD = F::AD;
+        v8bf aq[AD + 1][4];
+#pragma unroll
+        for (int d = 0; d < AD; ++d)
+          if (d < NA) load_a(d, aq[d]);
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+          if (f + AD < NA) load_a(f + AD, aq[(f + AD) % (AD + 1)]);
+          const v8bf* a_cur = aq[f % (AD + 1)];
+#pragma unroll
+          for (int j = 0; j < NFW; ++j)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[f][j] = mfma_bf16(a_cur[jj], bop[j][jj], acc[f][j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      auto compute_q = [&](int s) {
         const uint8_t* la = lds + (s % P) * L1::BUF;
         const uint8_t* lb = la + F::A_BYTES;
         const uint32_t* las = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
@@ -409,7 +477,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
           } else {
             aop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
           }
-          const uint32_t sw = AW ? *reinterpret_cast<const uint32_t*>(slot + ar * 16 + kq) : las[ar];
+          const uint32_t sw = AW ? *reinterpret_cast<const uint32_t*>(slot + ar * 16 + kq) : AS1 ? las[ar] : 0u;
           asc = (sw >> (8 * g)) & 0xFFu;
         };
         constexpr int AD = F::AD;
@@ -430,6 +498,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      };
+      auto compute = [&](int s) {
+        if constexpr (ADT == DT_BF16) compute_bf16(s);
+        else compute_q(s);
       };
 
       // ---- K loop: steps s+1 .. s+P-2 in flight while step s is computed
@@ -453,8 +525,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 
       // ---- epilogue: the item's output tile is staged in LDS by every wave
       {
-        uint8_t* st_codes = lds;                          // [BMW][OBS]
-        uint8_t* st_scales = lds + BMW * F::OBS;          // [BMW][4]: one byte per 32-column block
+        uint8_t* st_codes = lds;                          // [BM][OBS]
+        uint8_t* st_scales = lds + BM * F::OBS;           // [BM][4]: one byte per 32-column block
         const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
@@ -467,6 +539,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
             for (int h = 0; h < 2; ++h) {
               const float gs = acc[f][h][i], us = acc[f][2 + h][i];
               y[h] = ACT == ACT_SITUV2 ? situv2(gs, us, p.beta, inv_beta, p.linear_beta, inv_lb) : silu_mul(gs, us);
+            }
+            if constexpr (ADT == DT_BF16) {   // bf16 intermediate: an even lane stores its column and the next
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const uint32_t hb = f32_to_bf16_rne(y[h]);
+                const uint32_t hn = lane_xor1(hb);
+                const int c = 32 * wn + 16 * h + r16;
+                if ((r16 & 1) == 0) *reinterpret_cast<uint32_t*>(st_codes + row * F::OBS + 2 * c) = hb | (hn << 16);
+              }
+              continue;
             }
             const uint32_t amax =
                 row16_max_u32(max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu));
@@ -497,7 +579,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         if (!loader) {
           const int t = threadIdx.x - NLOAD * WAVE;
           constexpr int CPRO = F::OB / 16;
-          const size_t irow = ADT == DT_FP8 ? (size_t)I : (size_t)I / 2;   // intermediate row bytes
+          const size_t irow = ADT == DT_FP8 ? (size_t)I : ADT == DT_FP4 ? (size_t)I / 2 : (size_t)I * 2;   // intermediate row bytes
           for (int c = t; c < rows_used * CPRO; c += (GWAVES - NLOAD) * WAVE) {
             const int row = c / CPRO, part = c - row * CPRO;
             if ((unsigned)lds_v[row] < (unsigned)TK) {
@@ -506,7 +588,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
                   *reinterpret_cast<const uint4*>(st_codes + row * F::OBS + part * 16);
             }
           }
-          for (int row = t; row < rows_used; row += (GWAVES - NLOAD) * WAVE) {
+          for (int row = t; ADT != DT_BF16 && row < rows_used; row += (GWAVES - NLOAD) * WAVE) {
             if ((unsigned)lds_v[row] < (unsigned)TK) {
               const size_t R = (size_t)row_base + row;
               *reinterpret_cast<uint32_t*>(p.inter_s + R * (I / 32) + (size_t)nb * 4) =
@@ -516,12 +598,21 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         }
       }
     };
-    switch (n_af) {
-      case 0: run(std::integral_constant<int, 0>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 4: run(std::integral_constant<int, 4>{}); break;
-      case 6: run(std::integral_constant<int, 6>{}); break;
-      default: run(std::integral_constant<int, 8>{}); break;
+    if constexpr (MF == 4) {
+      switch (n_af) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
+      }
+    } else {
+      static_assert(MF == 8, "fragment counts");
+      switch (n_af) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        default: run(std::integral_constant<int, 8>{}); break;
+      }
     }
     lds_barrier();                                        // lds_v and the staging tile are reused
   }
@@ -752,9 +843,10 @@ template <int ADT, int STAGE>
 hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const int32_t* ngroups, hipStream_t s) {
   const int n_nblk = STAGE == 1 ? (2 * a.I) / BNW : a.D / BNW;
   const unsigned grid = (unsigned)(num_cus() / 8 * 8);    // one workgroup per CU, a multiple of 8
-  if (STAGE == 2)
+  if constexpr (STAGE == 2) {
+    static_assert(ADT != DT_BF16, "bf16 activations take the per-tile Stage2");
     grouped_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
-  else if (a.act == ACT_SITUV2)
+  } else if (a.act == ACT_SITUV2)
     grouped_stage1_kernel<ADT, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   else
     grouped_stage1_kernel<ADT, ACT_SILU><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
@@ -764,7 +856,9 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
 }  // namespace
 
 bool tiled_path_supported(const FusedArgs& a) {
-  return a.a_dtype != DT_BF16 && a.block_m == 32 && a.act != ACT_NONE && (2 * a.I) % BNW == 0 &&
+  // the A copies address the activation rows with 32-bit offsets
+  const int64_t x_bytes = (int64_t)a.T * a.D * (a.a_dtype == DT_BF16 ? 4 : a.a_dtype == DT_FP8 ? 2 : 1) / 2;
+  return a.block_m == 32 && a.act != ACT_NONE && (2 * a.I) % BNW == 0 && x_bytes < ((int64_t)1 << 32) &&
          a.D % 512 == 0;   // Stage1 takes whole 16-byte scale chunks; Stage2 needs D % BNW == 0
 }
 
@@ -773,11 +867,13 @@ hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipS
   if (a.stages & 1) {
     group_kernel<<<1, GROUP_THREADS, 0, s>>>(a.expert_ids, a.num_tiles, a.cap_tiles, groups, ngroups);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    err = a.a_dtype == DT_FP8 ? launch_grouped_stage<DT_FP8, 1>(a, groups, ngroups, s)
-                              : launch_grouped_stage<DT_FP4, 1>(a, groups, ngroups, s);
+    err = a.a_dtype == DT_FP8   ? launch_grouped_stage<DT_FP8, 1>(a, groups, ngroups, s)
+          : a.a_dtype == DT_FP4 ? launch_grouped_stage<DT_FP4, 1>(a, groups, ngroups, s)
+                                : launch_grouped_stage<DT_BF16, 1>(a, groups, ngroups, s);
     if (err != hipSuccess) return err;
   }
   if (a.stages & 2) {
+    if (a.a_dtype == DT_BF16) return hipErrorInvalidValue;   // bf16 activations take the per-tile Stage2
     err = a.a_dtype == DT_FP8 ? launch_grouped_stage<DT_FP8, 2>(a, groups, ngroups, s)
                               : launch_grouped_stage<DT_FP4, 2>(a, groups, ngroups, s);
     if (err != hipSuccess) return err;

@@ -61,13 +61,17 @@ SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
     (2, 64, 16, 512, 256, 0, 64, 32, "fp4", "situv2", 0.0),
     (4, 40, 8, 256, 384, 0, 40, 32, "bf16", "silu", 0.0),
     (8, 32, 4, 256, 256, 8, 8, 16, "fp8", "situv2", 0.0),        # expert-parallel shard
-    # >= 2048 tokens with fp8/fp4 activations and model_dim % 512 == 0: the tiled large-batch
+    # >= 2048 tokens with model_dim % 512 == 0: the tiled large-batch
     # stages (Stage1 scale chunks span 4 K steps: 7 chunks at 3584, 2 at 1024, 1 at 512)
     (2048, 16, 4, 512, 256, 0, 16, 32, "fp8", "situv2", 1.1),
     (2048, 16, 4, 512, 256, 0, 16, 32, "fp4", "situv2", 1.1),
     (2048, 24, 4, 1024, 512, 0, 24, 32, "fp8", "silu", 0.5),      # four Stage1 column blocks
     (2500, 40, 6, 1024, 128, 0, 40, 32, "fp4", "silu", 0.0),
     (3000, 64, 8, 1024, 384, 16, 24, 32, "fp8", "situv2", 0.0),
+    # bf16 activations from 2048 tokens: grouped Stage1 (128-row groups), per-tile Stage2
+    (2048, 16, 4, 512, 256, 0, 16, 32, "bf16", "situv2", 1.1),
+    (2500, 40, 6, 1024, 128, 0, 40, 32, "bf16", "silu", 0.0),
+    (3000, 64, 8, 1024, 384, 16, 24, 32, "bf16", "situv2", 0.0),
     # the same batch sizes with model_dim % 512 != 0 take the per-tile stages
     (2500, 40, 6, 256, 128, 0, 40, 32, "fp4", "silu", 0.0),
     (3000, 64, 8, 768, 384, 16, 24, 32, "fp8", "situv2", 0.0),
