@@ -263,11 +263,8 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
   const unsigned grid1 = (unsigned)((int64_t)a.cap_tiles * n1);
   const int n2 = (a.D + NWAVES * C::NF2 * 16 - 1) / (NWAVES * C::NF2 * 16);
   constexpr int T1 = C::KW * WAVE;
-  // grouped Stage1 for every activation dtype; grouped Stage2 for fp8 / fp4 (bf16 intermediate
-  // rows take the per-tile Stage2)
   const bool tiled = tiled_path_supported(a);
-  const bool tiled1 = tiled && a.T >= TILED_MIN_TOKENS_S1;
-  const bool tiled2 = ADT != DT_BF16 && tiled && a.T >= TILED_MIN_TOKENS_S2;
+  const bool tiled1 = tiled && a.T >= TILED_MIN_TOKENS_S1, tiled2 = tiled && a.T >= TILED_MIN_TOKENS_S2;
   if (tiled1 || (tiled2 && !(a.stages & 1))) {
     FusedArgs t = a;
     t.stages = a.stages & ((tiled1 ? 1 : 0) | (tiled2 ? 2 : 0));

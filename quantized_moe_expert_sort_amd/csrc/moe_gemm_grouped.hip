@@ -45,9 +45,7 @@ constexpr int GT = 8;                         // sort tiles (of 32 rows) per gro
 constexpr int GTHREADS = 512;
 constexpr int GWAVES = GTHREADS / WAVE;       // 8
 constexpr int WM = 2, WN = 4;                 // wave grid: rows x weight rows
-constexpr int BMW = GT * 32;                  // rows per group: 256
 constexpr int BNW = 256;                      // weight rows per column block
-constexpr int MFW = BMW / WM / 16;            // 16-row A fragments per wave: 8
 constexpr int NFW = BNW / WN / 16;            // 16-row B fragments per wave: 4
 static_assert(WM * WN == GWAVES, "wave grid");
 
@@ -225,9 +223,9 @@ __device__ __forceinline__ int swz_slot(int row, int part) {
 
 constexpr int NLOAD = 4;                      // loader waves
 
-// bf16 activations (Stage1 only): an item takes one half of a group (up to 4 tiles, 128 rows),
-// so the 256-byte A row pieces of a K step leave room for three buffers; the B side (fp4 rows,
-// scale chunks) is that of fp8 / fp4.
+// bf16 activations / intermediate rows: an item takes one part of a group (up to 4 tiles, 128
+// rows), so the 256-byte A row pieces of a K step leave room for three buffers; the B side
+// (fp4 rows and their scales) is that of fp8 / fp4.
 template <int ADT>
 struct GFmt {
   static constexpr int GTA = ADT == DT_BF16 ? GT / 2 : GT;   // sort tiles per item, at most
@@ -239,7 +237,7 @@ struct GFmt {
   static constexpr int AD = ADT == DT_FP8 ? 2 : ADT == DT_FP4 ? 3 : 1;   // A fragments read ahead of the MFMAs
   static constexpr int A_BYTES = BM * KA;
   static constexpr int B_BYTES = BNW * 64;
-  static constexpr int BUF = A_BYTES + B_BYTES + (BMW + BNW) * 4;
+  static constexpr int BUF = A_BYTES + B_BYTES + (BM + BNW) * 4;   // Stage2: + per-step scale dwords
   static constexpr int A_IPL = A_BYTES / 1024 / NLOAD;    // A copy instructions per loader per step
   static constexpr int B_IPL = B_BYTES / 1024 / NLOAD;
   static constexpr int ROWS_PER_AI = 1024 / KA;           // A rows covered by one instruction
@@ -442,10 +440,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         for (int f = 0; f < NA; ++f) {
           if (f + AD < NA) load_a(f + AD, aq[(f + AD) % (AD + 1)]);
           const v8bf* a_cur = aq[f % (AD + 1)];
+          // sub-step outer: consecutive MFMAs write different accumulators, so none waits for
+          // the one before it (a wave alone on its SIMD would stall on a dependent chain)
 #pragma unroll
-          for (int j = 0; j < NFW; ++j)
+          for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) acc[f][j] = mfma_bf16(a_cur[jj], bop[j][jj], acc[f][j]);
+            for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_bf16(a_cur[jj], bop[j][jj], acc[f][j]);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -646,7 +646,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
                                                                      const int32_t* __restrict__ num_groups,
                                                                      int n_nblk) {
   using F = GFmt<ADT>;
-  constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P;
+  constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P, BM = F::BM, MF = F::MF;
+  constexpr bool HAS_AS = ADT != DT_BF16;
+  constexpr int PARTS = GT / F::GTA;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[P * F::BUF];
 
   const int D = p.D, I = p.I;
@@ -662,21 +664,30 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
 
   const int ng = ld_const(num_groups);
   const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
-  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_nblk;
+  const int per_group = PARTS * n_nblk;                   // items (part, column block) per group
+  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * per_group;
 
   struct Src {
     const uint8_t *a, *as, *b, *bs;
     uint32_t a_off[F::A_IPL], b_off[F::B_IPL], as_off, bs_off;
     int n_ai, rows_used, row_base, nb, per_step;
-    bool as_on;
+    bool as_on, b_on;
   };
   // copy sources of item `local`: A the group's intermediate rows (rows past the group read its
   // first row; their results are not stored), B output rows [nb*BNW, nb*BNW + BNW) of w2
+  // (bf16: a group is taken in two parts of ceil(n/2) and floor(n/2) tiles; a one-tile group's
+  // empty part copies nothing)
   auto make = [&](int local, Src& q) {
-    const int gl = local / n_nblk;
-    q.nb = local - gl * n_nblk;
+    const int gl = local / per_group, rem = local - gl * per_group;
+    const int part = rem / n_nblk;
+    q.nb = rem - part * n_nblk;
     const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
-    const int tile0 = ld_const(gp), ntiles = ld_const(gp + 1);
+    int tile0 = ld_const(gp), ntiles = ld_const(gp + 1);
+    if (PARTS == 2) {
+      const int h0 = (ntiles + 1) >> 1;
+      tile0 += part ? h0 : 0;
+      ntiles = part ? ntiles - h0 : h0;
+    }
     q.rows_used = ntiles * 32;
     q.row_base = tile0 * 32;
     const int e = ld_const(p.expert_ids + tile0);
@@ -701,11 +712,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
       q.b_off[i] = (uint32_t)(q.nb * BNW + row) * (uint32_t)(I / 2) + part * 16;
     }
     const int sc_row = lw * WAVE + lane;
-    q.as_on = lw * WAVE < q.rows_used;
+    q.as_on = HAS_AS && lw * WAVE < q.rows_used;
+    q.b_on = q.rows_used > 0;
     q.as_off = (uint32_t)(sc_row < q.rows_used ? sc_row : 0) * (uint32_t)(I / 32);
     q.bs_off = (uint32_t)(q.nb * BNW + sc_row) * (uint32_t)(I / 32);
     q.n_ai = n_ai;
-    q.per_step = n_ai + F::B_IPL + (q.as_on ? 1 : 0) + 1;
+    q.per_step = n_ai + (q.b_on ? F::B_IPL + 1 : 0) + (q.as_on ? 1 : 0);
   };
   auto issue = [&](const Src& q, int s, int buf) {
     const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * F::BUF);
@@ -714,14 +726,15 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
 #pragma unroll
     for (int i = 0; i < F::A_IPL; ++i)
       if (i < q.n_ai) dma16(ab, q.a_off[i], L + (i * NLOAD + lw) * 1024);
+    if (!q.b_on) return;
 #pragma unroll
     for (int i = 0; i < F::B_IPL; ++i)
       dma16(bb, q.b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
     if (q.as_on) dma4(q.as + s * 4, q.as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
-    dma4(q.bs + s * 4, q.bs_off, L + F::A_BYTES + F::B_BYTES + BMW * 4 + lw * 256);
+    dma4(q.bs + s * 4, q.bs_off, L + F::A_BYTES + F::B_BYTES + BM * 4 + lw * 256);
   };
 
-  const int arow0 = 128 * wm;
+  const int arow0 = (BM / WM) * wm;
   Src cur, nxt;
   int local = local0;
   if (local < items_here) {
@@ -736,7 +749,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
   for (; local < items_here; local += stride) {
     const bool has_next = local + stride < items_here;
     if (has_next) make(local + stride, nxt);
-    const int n_af = max(0, min(MFW, (cur.rows_used - arow0) / 16));
+    const int n_af = max(0, min(MF, (cur.rows_used - arow0) / 16));
 
     auto run = [&](auto na_c) {
       constexpr int NA = decltype(na_c)::value;
@@ -746,11 +759,53 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
 #pragma unroll
         for (int j = 0; j < NFW; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-      auto compute = [&](int buf) {
+      // bf16 intermediate rows: lane group g takes K [32 g, 32 g + 32) of the step for both
+      // operands (one weight scale block), four 32-deep bf16 MFMAs per 16 x 16 block, the fp4
+      // weight rows widened to bf16 with the scaled converts
+      auto compute_bf16 = [&](int buf) {
+        const uint8_t* la = lds + buf * F::BUF;
+        const uint8_t* lb = la + F::A_BYTES;
+        const uint32_t* lbs = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES) + BM;
+        v8bf wop[NFW][4];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          const int br = 64 * wn + (j >> 1) * 32 + 8 * (r16 >> 2) + 4 * (j & 1) + (r16 & 3);
+          const uint4 q = *reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16);
+          const float sc = e8m0_to_float((lbs[br] >> (8 * g)) & 0xFFu);
+          wop[j][0] = fp4x8_to_bf16(q.x, sc);
+          wop[j][1] = fp4x8_to_bf16(q.y, sc);
+          wop[j][2] = fp4x8_to_bf16(q.z, sc);
+          wop[j][3] = fp4x8_to_bf16(q.w, sc);
+        }
+        auto load_x = [&](int f, v8bf* x) {
+          const int ar = arow0 + 16 * f + r16;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint4 q = *reinterpret_cast<const uint4*>(la + swz_slot<16>(ar, 4 * g + jj) * 16);
+            x[jj] = as_bf16x8(q.x, q.y, q.z, q.w);
+          }
+        };
+        v8bf x_cur[4];
+        load_x(0, x_cur);
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+          v8bf x_nxt[4] = {x_cur[0], x_cur[1], x_cur[2], x_cur[3]};
+          if (f + 1 < NA) load_x(f + 1, x_nxt);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_bf16(wop[j][jj], x_cur[jj], acc[f][j]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) x_cur[jj] = x_nxt[jj];
+        }
+      };
+
+      auto compute_q = [&](int buf) {
         const uint8_t* la = lds + buf * F::BUF;
         const uint8_t* lb = la + F::A_BYTES;
         const uint32_t* las = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
-        const uint32_t* lbs = las + BMW;
+        const uint32_t* lbs = las + BM;
         v8i wop[NFW];
         uint32_t wsc[NFW];
 #pragma unroll
@@ -785,6 +840,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
           xs_cur = xs_nxt;
         }
       };
+      auto compute = [&](int buf) {
+        if constexpr (ADT == DT_BF16) compute_bf16(buf);
+        else compute_q(buf);
+      };
 
       for (int s = 0; s < S; ++s) {
         // a loader's copies of step s are done once at most (those issued after them) remain:
@@ -815,12 +874,20 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
       }
       n_st = 2 * NA;
     };
-    switch (n_af) {
-      case 0: run(std::integral_constant<int, 0>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 4: run(std::integral_constant<int, 4>{}); break;
-      case 6: run(std::integral_constant<int, 6>{}); break;
-      default: run(std::integral_constant<int, 8>{}); break;
+    if constexpr (MF == 4) {
+      switch (n_af) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
+      }
+    } else {
+      switch (n_af) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        default: run(std::integral_constant<int, 8>{}); break;
+      }
     }
     cur = nxt;
   }
@@ -844,7 +911,6 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
   const int n_nblk = STAGE == 1 ? (2 * a.I) / BNW : a.D / BNW;
   const unsigned grid = (unsigned)(num_cus() / 8 * 8);    // one workgroup per CU, a multiple of 8
   if constexpr (STAGE == 2) {
-    static_assert(ADT != DT_BF16, "bf16 activations take the per-tile Stage2");
     grouped_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   } else if (a.act == ACT_SITUV2)
     grouped_stage1_kernel<ADT, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
@@ -873,9 +939,9 @@ hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipS
     if (err != hipSuccess) return err;
   }
   if (a.stages & 2) {
-    if (a.a_dtype == DT_BF16) return hipErrorInvalidValue;   // bf16 activations take the per-tile Stage2
-    err = a.a_dtype == DT_FP8 ? launch_grouped_stage<DT_FP8, 2>(a, groups, ngroups, s)
-                              : launch_grouped_stage<DT_FP4, 2>(a, groups, ngroups, s);
+    err = a.a_dtype == DT_FP8   ? launch_grouped_stage<DT_FP8, 2>(a, groups, ngroups, s)
+          : a.a_dtype == DT_FP4 ? launch_grouped_stage<DT_FP4, 2>(a, groups, ngroups, s)
+                                : launch_grouped_stage<DT_BF16, 2>(a, groups, ngroups, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
