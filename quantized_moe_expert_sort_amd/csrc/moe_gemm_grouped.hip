@@ -291,28 +291,28 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
   const uint32_t lds0 = lds_addr(lds);
   const uint32_t slot0 = lds0 + P * L1::BUF;
 
-  // groups gi = xcd, xcd + 8, ... run on XCD xcd; item (group, part, column block), where a
-  // bf16 group is taken in two parts of at most GTA tiles.  The items of one group are
-  // consecutive, so they run at the same time on CUs of one XCD and fetch the group's
-  // activation rows and weight rows into its L2 once.
+  // groups gi = xcd, xcd + 8, ... run on XCD xcd; item (part, group, column block), where a
+  // bf16 group of more than GTA tiles is taken in two parts.  The column blocks of a group are
+  // consecutive items, so they run at the same time on CUs of one XCD and fetch the group's
+  // activation rows into its L2 once; second parts (empty for most small groups) come last.
   constexpr int PARTS = GT / F::GTA;
   const int ng = *num_groups;
   const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
-  const int per_group = PARTS * n_nblk;
-  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * per_group;
+  const int per_part = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_nblk;
+  const int items_here = PARTS * per_part;
 
   for (int local = local0; local < items_here; local += stride) {
-    const int gl = local / per_group, rem = local - gl * per_group;
-    const int part = rem / n_nblk, nb = rem - part * n_nblk;
+    const int part = local >= per_part ? 1 : 0, rem = local - part * per_part;
+    const int gl = rem / n_nblk, nb = rem - gl * n_nblk;
     const int gi = gl * 8 + xcd;
     const int2 grp = groups[gi];
     int tile0 = grp.x, ntile = grp.y;
-    if (PARTS == 2) {                                     // parts of ceil(n/2) and floor(n/2) tiles
-      const int h0 = (grp.y + 1) >> 1;
+    if (PARTS == 2) {   // up to GTA tiles: one part; more: parts of ceil(n/2) and floor(n/2) tiles
+      const int h0 = grp.y <= F::GTA ? grp.y : (grp.y + 1) >> 1;
       tile0 += part ? h0 : 0;
       ntile = part ? grp.y - h0 : h0;
     }
-    if (ntile == 0) continue;                             // a one-tile group's empty part
+    if (ntile == 0) continue;                             // the empty second part of a small group
     const int rows_used = ntile * 32;
     const int e = p.expert_ids[tile0];
     const int row_base = tile0 * 32;                      // first layout row of the group
@@ -664,8 +664,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
 
   const int ng = ld_const(num_groups);
   const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
-  const int per_group = PARTS * n_nblk;                   // items (part, column block) per group
-  const int items_here = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * per_group;
+  const int per_part = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_nblk;   // items (part, group, column block)
+  const int items_here = PARTS * per_part;
 
   struct Src {
     const uint8_t *a, *as, *b, *bs;
@@ -675,16 +675,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
   };
   // copy sources of item `local`: A the group's intermediate rows (rows past the group read its
   // first row; their results are not stored), B output rows [nb*BNW, nb*BNW + BNW) of w2
-  // (bf16: a group is taken in two parts of ceil(n/2) and floor(n/2) tiles; a one-tile group's
-  // empty part copies nothing)
+  // (bf16: a group of up to GTA tiles is one part, a larger one two parts of ceil(n/2) and
+  // floor(n/2) tiles; the empty second part of a small group copies nothing)
   auto make = [&](int local, Src& q) {
-    const int gl = local / per_group, rem = local - gl * per_group;
-    const int part = rem / n_nblk;
-    q.nb = rem - part * n_nblk;
+    const int part = local >= per_part ? 1 : 0, rem = local - part * per_part;
+    const int gl = rem / n_nblk;
+    q.nb = rem - gl * n_nblk;
     const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
     int tile0 = ld_const(gp), ntiles = ld_const(gp + 1);
     if (PARTS == 2) {
-      const int h0 = (ntiles + 1) >> 1;
+      const int h0 = ntiles <= F::GTA ? ntiles : (ntiles + 1) >> 1;
       tile0 += part ? h0 : 0;
       ntiles = part ? ntiles - h0 : h0;
     }
