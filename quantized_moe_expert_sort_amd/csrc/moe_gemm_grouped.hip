@@ -6,7 +6,9 @@
 // expert's tiles are split into groups of balanced size), so each weight byte fetched serves
 // up to GT*32 rows, and a column block is BNW weight rows.  Eight waves in a 2 (rows) x 4
 // (weight rows) grid each compute a 128 x 64 sub-tile with v_mfma_scale_f32_16x16x128_f8f6f4
-// (fp8 x fp4 or fp4 x fp4); 16-row fragments past the group's rows are skipped.  Waves w and
+// (fp8 x fp4 or fp4 x fp4); 16-row fragments past the group's rows are skipped.  bf16
+// activations take items of at most 128 rows (64 x 64 per wave) and v_mfma_f32_16x16x32_bf16 on
+// weights widened to bf16 in registers.  Waves w and
 // w + 4 share a SIMD and own the two row halves, so every SIMD does the same work whatever
 // the group's row count.
 //
