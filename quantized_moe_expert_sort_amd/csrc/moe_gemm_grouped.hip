@@ -274,7 +274,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
   constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P, BM = F::BM, MF = F::MF;
   constexpr bool AW = L1::AW, AS1 = L1::AS1, HAS_AS = AW || AS1;
   static_assert(F::A_IPL * NLOAD * 1024 == F::A_BYTES && F::B_IPL * NLOAD * 1024 == F::B_BYTES, "copy split");
-  static_assert((!HAS_AS || BM == NLOAD * WAVE) && BNW == NLOAD * WAVE, "one scale copy of each operand per loader");
+  static_assert(BM <= NLOAD * WAVE && BNW == NLOAD * WAVE, "at most one scale copy of each operand per loader");
   static_assert(BM * (F::OBS + 4) <= P * L1::BUF, "staging fits");
   static_assert(P <= 5, "a chunk slot is refilled only after the four steps of its previous chunk");
 
@@ -361,8 +361,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
     }
     // scales: loader lw copies those of A rows and of B rows [64 lw, 64 lw + 64)
     const int sc_row = lw * WAVE + lane;
-    const bool as_on = HAS_AS && lw * WAVE < rows_used;
-    const uint32_t as_off = HAS_AS ? a_src_index(sc_row) * (uint32_t)(K / 32) : 0u;
+    const bool as_on = HAS_AS && lw * WAVE < rows_used;   // rows_used <= BM
+    const uint32_t as_off = HAS_AS && sc_row < BM ? a_src_index(sc_row) * (uint32_t)(K / 32) : 0u;
     const uint32_t bs_off = (uint32_t)b_row(sc_row) * (uint32_t)(K / 32);
     // copy instructions a loader issues for step s: the chunks travel with steps 0, 4, 8, ...
     const int n_data = n_ai + F::B_IPL + (AS1 && as_on ? 1 : 0);

@@ -72,6 +72,7 @@ SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
     (2048, 16, 4, 512, 256, 0, 16, 32, "bf16", "situv2", 1.1),
     (2500, 40, 6, 1024, 128, 0, 40, 32, "bf16", "silu", 0.0),
     (3000, 64, 8, 1024, 384, 16, 24, 32, "bf16", "situv2", 0.0),
+    (2048, 64, 5, 512, 256, 0, 64, 32, "bf16", "situv2", 0.0),    # ~5-tile groups: parts of 3 + 2 tiles
     # the same batch sizes with model_dim % 512 != 0 take the per-tile stages
     (2500, 40, 6, 256, 128, 0, 40, 32, "fp4", "silu", 0.0),
     (3000, 64, 8, 768, 384, 16, 24, 32, "fp8", "situv2", 0.0),
