@@ -415,7 +415,7 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(wl, host)
 
-    pages = PAGES_US.get((wl.a_dtype, wl.tokens))
+    pages = PAGES_US.get((wl.a_dtype, wl.tokens), PAGES_TIER_US.get(wl.name))
     line = {
         "metric": METRIC, "value": s["us_per_step"], "unit": "us/call", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 6),
