@@ -361,7 +361,7 @@ def main():
         if key not in weights:
             log(f"generating weights E={w.experts} D={w.model_dim} I={w.inter_dim}")
             host = gen.make_weights(w.seed, w.experts, w.model_dim, w.inter_dim)
-            weights[key] = (host, tuple(torch.from_numpy(a).cuda() for a in host))
+            weights[key] = (host, qm.device_weights(*host))
         return weights[key]
 
     host, dev_w = weights_for(wl)

@@ -14,6 +14,7 @@
  *                    tanh evaluated as 2*sigmoid(2x)-1 (PR 4471 "Technical Details");
  *                    the intermediate re-encoded in the activation dtype; Stage2: MXFP4
  *                    down-projection, times the router weight, summed into each token's row.
+ *   moe_pack_w1 reorders the Stage1 weights once into the layout moe_fused streams.
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library never
@@ -186,11 +187,25 @@ moe_status_t moe_sort(const int32_t *topk_ids, const float *topk_w, int32_t toke
 moe_status_t moe_quant_act(const uint16_t *x_bf16, int64_t rows, int64_t cols, int32_t dt,
                            void *q_out, uint8_t *scale_out, void *stream);
 
+/* moe_pack_w1 -- reorder the Stage1 weights once into the layout moe_fused reads (a one-time
+ * weight preparation, as the pages' kernels read pre-shuffled weights: PR 5118 "Summary").
+ *   w1         [E, 2I, D/2] fp4x2, row-major (rows 0..I-1 gate, I..2I-1 up).
+ *   w1_packed  E*2I*D/2 bytes, caller-owned, not aliasing w1: 1 KB blocks (e, f, s) for row
+ *              group f < 2I/16 and K step s < D/128, in that order (s fastest); byte
+ *              16*(16*g + r) + b of a block is byte 64*s + 16*g + b of row 16*f + r of expert e
+ *              (g < 4, r < 16, b < 16).  The e8m0 scales keep their layout.
+ * Shapes as moe_fused: D % 128 == 0, I % 128 == 0 (else MOE_ERR_UNSUPPORTED); E >= 1.
+ * Asynchronous on `stream`; a pure copy, bit-exact. */
+moe_status_t moe_pack_w1(const uint8_t *w1, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
+                         uint8_t *w1_packed, void *stream);
+
 /* moe_fused -- Stage1 + Stage2 over a layout from moe_sort.
  *   x         activations [tokens, D]: bf16 (a_dtype BF16), fp8 bytes (FP8) or fp4x2 bytes
  *             [tokens, D/2] (FP4), as moe_quant_act writes them.
  *   x_scale   [tokens, D/32] e8m0 for FP8 / FP4; must be NULL for BF16.
- *   w1, w1_scale  [E, 2I, D/2] fp4x2 and [E, 2I, D/32] e8m0: rows 0..I-1 gate, I..2I-1 up.
+ *   w1        Stage1 weights [E, 2I, D/2] fp4x2 (rows 0..I-1 gate, I..2I-1 up) in the packed
+ *             layout moe_pack_w1 writes.
+ *   w1_scale  [E, 2I, D/32] e8m0, row-major.
  *   w2, w2_scale  [E, D, I/2] fp4x2 and [E, D, I/32] e8m0.
  *   topk_w    [tokens, topk] fp32 router weights; row v of the layout is scaled by topk_w[v].
  *   layout    from moe_sort with the same tokens/topk/E; cap_tiles and block_m as there.
@@ -205,9 +220,9 @@ moe_status_t moe_quant_act(const uint16_t *x_bf16, int64_t rows, int64_t cols, i
  * Shapes: D % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED: every K step is one
  * 128-deep block-scaled MFMA); E >= 1.  Stage1 uses fp32 accumulation; the intermediate is
  * stored as bf16 (BF16) or re-encoded with the moe_quant_act rule (FP8, FP4); Stage2
- * accumulates in fp32, stores each routed row's weighted output (fp32 for BF16, bf16
- * otherwise), and the combine sums each token's rows in ascending k in fp32 and rounds to
- * bf16: the result is deterministic, and the single-launch and per-stage paths give the same
+ * accumulates in fp32, stores each routed row's output in bf16 (scaled by its router weight
+ * in Stage2, or in the combine after the large-batch Stage2), and the combine sums each token's
+ * rows in ascending k in fp32 and rounds to bf16: the result is deterministic, and the single-launch and per-stage paths give the same
  * bits.  layout->row_of must be set. */
 moe_status_t moe_fused(const void *x, const uint8_t *x_scale, int32_t a_dtype,
                        const uint8_t *w1, const uint8_t *w1_scale,

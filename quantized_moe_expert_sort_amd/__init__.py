@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
 SORT_CHUNK = 4096
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
-EXPORTS = ("moe_sort", "moe_quant_act", "moe_fused", "moe_last_hip_error")
+EXPORTS = ("moe_sort", "moe_quant_act", "moe_pack_w1", "moe_fused", "moe_last_hip_error")
 
 
 class MoeError(RuntimeError):
@@ -62,6 +62,8 @@ def lib():
         L.moe_fused.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(Layout), i32, i32, i32,
                                 i32, i32, ctypes.POINTER(ActParams), vp, vp, sz, i32, vp]
         L.moe_fused.restype = i32
+        L.moe_pack_w1.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.moe_pack_w1.restype = i32
         L.moe_last_hip_error.argtypes = []
         L.moe_last_hip_error.restype = i32
         _lib = L
@@ -171,6 +173,23 @@ def moe_sort(topk_ids, topk_w, expert_begin, num_local_experts, block_m, with_we
     return layout
 
 
+def moe_pack_w1(w1, out=None):
+    """Stage1 weights [E, 2I, D/2] uint8 (row-major) -> the packed layout moe_fused reads."""
+    E, rows, half_d = w1.shape
+    if out is None:
+        out = torch.empty_like(w1)
+    _check("moe_pack_w1", lib().moe_pack_w1(_ptr(w1), E, half_d * 2, rows // 2, _ptr(out), _stream()))
+    return out
+
+
+def device_weights(w1, w1s, w2, w2s, device="cuda"):
+    """Host MXFP4 weights (numpy, row-major) -> the device tuple moe_fused takes (w1 packed)."""
+    w1_d, w1s_d, w2_d, w2s_d = (torch.from_numpy(a).to(device) for a in (w1, w1s, w2, w2s))
+    packed = moe_pack_w1(w1_d)
+    del w1_d
+    return packed, w1s_d, w2_d, w2s_d
+
+
 def moe_quant_act(x_bf16, dt, q=None, scale=None):
     """bf16 [rows, cols] -> (codes, e8m0 scales); dt is "fp8" or "fp4"."""
     d = DTYPES[dt] if isinstance(dt, str) else dt
@@ -185,7 +204,7 @@ def moe_quant_act(x_bf16, dt, q=None, scale=None):
 
 def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, num_local_experts,
               act="situv2", beta=None, linear_beta=None, out=None, ws=None, stages=STAGE_ALL):
-    """Stage1 + Stage2 over a layout from moe_sort; returns out [T, D] bf16 (or, for
+    """Stage1 + Stage2 over a layout from moe_sort (w1 packed by moe_pack_w1); returns out [T, D] bf16 (or, for
     act="none_test", the workspace tensor holding the raw gate/up sums).  stages selects
     STAGE_1, STAGE_2 (reusing the intermediate a STAGE_1 call left in the same ws) or both."""
     d = DTYPES[a_dtype] if isinstance(a_dtype, str) else a_dtype

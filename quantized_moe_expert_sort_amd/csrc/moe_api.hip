@@ -53,6 +53,15 @@ moe_status_t moe_sort(const int32_t* topk_ids, const float* topk_w, int32_t toke
                                      layout->block_m, L, ws, (hipStream_t)stream));
 }
 
+moe_status_t moe_pack_w1(const uint8_t* w1, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
+                         uint8_t* w1_packed, void* stream) {
+  if (!w1 || !w1_packed || w1 == w1_packed) return MOE_ERR_INVALID_ARG;
+  if (num_experts < 1 || model_dim <= 0 || inter_dim <= 0) return MOE_ERR_INVALID_ARG;
+  if (model_dim % 128 != 0 || inter_dim % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)num_experts * 2 * inter_dim * (model_dim / 2) / 16 >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_pack_w1(w1, w1_packed, num_experts, model_dim, inter_dim, (hipStream_t)stream));
+}
+
 moe_status_t moe_quant_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, int32_t dt, void* q_out,
                            uint8_t* scale_out, void* stream) {
   if (dt != MOE_DT_FP8_E4M3 && dt != MOE_DT_FP4_E2M1) return MOE_ERR_INVALID_ARG;

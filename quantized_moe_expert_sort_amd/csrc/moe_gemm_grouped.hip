@@ -351,13 +351,13 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
       a_off[i] = a_src_index(row) * (uint32_t)a_rowbytes + part * 16;
       n_ai += j * F::ROWS_PER_AI < rows_used;
     }
+    // B instruction j copies tile rows [16 j, 16 j + 16): weight rows b_row(16 j) .. + 15, one
+    // 1 KB block of packed w1 per step, to LDS bytes [1024 j, 1024 j + 1024) in the same order
     uint32_t b_off[F::B_IPL];
 #pragma unroll
     for (int i = 0; i < F::B_IPL; ++i) {
       const int j = i * NLOAD + lw;
-      const int q = j * WAVE + lane;
-      const int row = q / 4, part = swz_slot<4>(row, q % 4) - row * 4;
-      b_off[i] = (uint32_t)b_row(row) * (uint32_t)(K / 2) + part * 16;
+      b_off[i] = (uint32_t)(b_row(16 * j) / 16) * (uint32_t)(S * 1024) + 16 * lane;
     }
     // scales: loader lw copies those of A rows and of B rows [64 lw, 64 lw + 64)
     const int sc_row = lw * WAVE + lane;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
       }
       const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * L1::BUF);
       const uint8_t* ab = a_base + s * KA;
-      const uint8_t* bb = b_base + s * 64;
+      const uint8_t* bb = b_base + s * 1024;
 #pragma unroll
       for (int i = 0; i < F::A_IPL; ++i)
         if (i < n_ai) dma16(ab, a_off[i], L + (i * NLOAD + lw) * 1024);
@@ -417,7 +417,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
           const int br = b_frag_row(j) + r16;
-          const uint4 q = *reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16);
+          // packed B block of rows b_frag_row(j) .. + 15: lane (r16, g) at 16 (16 g + r16)
+          const uint4 q = *reinterpret_cast<const uint4*>(lb + b_frag_row(j) * 64 + lane * 16);
           const uint32_t bs = (*reinterpret_cast<const uint32_t*>(slot + L1::A_SLOT + br * 16 + kq) >> (8 * g)) & 0xFFu;
           const float sc = e8m0_to_float(bs);
           bop[j][0] = fp4x8_to_bf16(q.x, sc);
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
           const int br = b_frag_row(j) + r16;
-          bop[j] = fp4_operand_lo(*reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16));
+          bop[j] = fp4_operand_lo(*reinterpret_cast<const uint4*>(lb + b_frag_row(j) * 64 + lane * 16));
           bsc[j] = (*reinterpret_cast<const uint32_t*>(slot + L1::A_SLOT + br * 16 + kq) >> (8 * g)) & 0xFFu;
         }
         // A fragment f+AD is read from LDS while the MFMAs of fragment f run (an LDS read

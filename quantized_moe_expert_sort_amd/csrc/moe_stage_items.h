@@ -116,7 +116,10 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     const int c = 16 * j + r16;
     const int n = (c < NI) ? nb * NI + c : I + nb * NI + c - NI;
     const size_t wr = (size_t)e * 2 * I + n;
-    brow[j] = p.w1 + wr * (D / 2);
+    // packed w1 (moe_pack.hip): the 1 KB block of row group n / 16 and K step s holds the 16 rows
+    // x 64 bytes in lane order, lane (r16, g) at bytes 16 (16 g + r16); consecutive steps are
+    // consecutive blocks
+    brow[j] = p.w1 + ((size_t)e * (2 * I / 16) + n / 16) * (size_t)(D / 128) * 1024 + 16 * (16 * g + r16);
     bsrow[j] = p.w1s + wr * (D / 32);
   }
 
@@ -150,12 +153,12 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     // one base address per fragment; the steps are immediate offsets of the loads
     const uint8_t* bbase[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bbase[j] = brow[j] + s0 * 64 + 16 * g;
+    for (int j = 0; j < NB; ++j) bbase[j] = brow[j] + s0 * 1024;
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       if (FULL || s0 + i < s_end)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 64);
+        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 1024);
     // every load of the chunk is issued before the first wait (the scheduler would otherwise
     // sink the later steps' loads below the first MFMAs, a second memory round trip)
     __builtin_amdgcn_sched_barrier(0);
@@ -228,12 +231,12 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     stage_group(0, s0, n_s);
     const uint8_t* bbase[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bbase[j] = brow[j] + s0 * 64 + 16 * g;
+    for (int j = 0; j < NB; ++j) bbase[j] = brow[j] + s0 * 1024;
 #pragma unroll
     for (int i = 0; i < PF; ++i)
       if (FULL || i < n_s)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 64);
+        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 1024);
     __builtin_amdgcn_sched_barrier(0);
     // the copies were issued before the PF*NB weight loads: once at most that many loads are
     // outstanding, the staged rows are in LDS

@@ -117,6 +117,17 @@ def test_quant_validation():
     assert q(P, 0, 64, 2, P, P, None) == OK             # no rows: nothing to do
 
 
+@no_gpu
+def test_pack_validation():
+    f = qm.lib().moe_pack_w1
+    P2 = ctypes.c_void_p(8192)
+    assert f(P, 2, 256, 128, P, None) == INVALID        # in place
+    assert f(None, 2, 256, 128, P2, None) == INVALID
+    assert f(P, 0, 256, 128, P2, None) == INVALID       # no experts
+    assert f(P, 2, 192, 128, P2, None) == UNSUPPORTED   # model_dim % 128
+    assert f(P, 2, 256, 64, P2, None) == UNSUPPORTED    # inter_dim % 128
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(qm, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(qm, "_lib", None)

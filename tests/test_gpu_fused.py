@@ -85,7 +85,7 @@ def test_fused_small_full_output(T, Er, K, D, I, eb, E, bm, a_dtype, act, zipf):
     ids, w = gen.make_routing(seed, T, Er, K, zipf)
     x = gen.make_x(seed, T, D)
     w1, w1s, w2, w2s = gen.make_weights(seed, E, D, I, experts=range(eb, eb + E))
-    wd = tuple(dev(a) for a in (w1, w1s, w2, w2s))
+    wd = qm.device_weights(w1, w1s, w2, w2s)
     print(f"fused small T={T} E={E} D={D} I={I} bm={bm} {a_dtype} {act}", flush=True)
     out, _ = run_gpu(x, ids, w, wd, eb, E, bm, a_dtype, act)
     got = out.float().cpu().numpy().astype(np.float64)
@@ -111,7 +111,7 @@ def test_stage1_exact_integer_sums(a_dtype, bm):
     w2s = np.full((E, D, I // 32), 127, np.uint8)
     ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
     w = np.ones((T, K), np.float32)
-    wd = tuple(dev(a) for a in (w1, w1s, w2, w2s))
+    wd = qm.device_weights(w1, w1s, w2, w2s)
     ws, lay = run_gpu(x, ids, w, wd, 0, E, bm, a_dtype, act="none_test")
     off = qm.fused_debug_offset(T, D, I, lay.cap, bm, qm.DTYPES[a_dtype])
     rows = lay.cap * bm
@@ -139,7 +139,7 @@ def weights_for(wl):
     if key not in _WEIGHTS:
         _WEIGHTS.clear()
         host = gen.make_weights(wl.seed, wl.experts, wl.model_dim, wl.inter_dim)
-        _WEIGHTS[key] = (host, tuple(dev(a) for a in host))
+        _WEIGHTS[key] = (host, qm.device_weights(*host))
     return _WEIGHTS[key]
 
 

@@ -32,7 +32,7 @@ def problem(T, Er, K, D, I, eb, E, a_dtype, zipf=0.0, seed=None):
     else:
         xa, xs = qm.moe_quant_act(x_d, a_dtype)
     return dict(ids=ids, w=w, x=x, host_w=host_w, ids_d=dev(ids), w_d=dev(w), xa=xa, xs=xs,
-                wd=tuple(dev(a) for a in host_w))
+                wd=qm.device_weights(*host_w))
 
 
 def fused(pb, lay, eb, E, a_dtype, act="situv2"):
