@@ -246,8 +246,9 @@ struct Cfg {
   // tokens; bf16: 32, Stage1 30% faster at 8192 tokens); slower at 16-row tiles
   static constexpr int NI = BM == 32 ? (ADT == DT_BF16 ? 32 : 64) : (ADT == DT_BF16 ? 16 : 32);
   static constexpr int KW = 4;                                // waves splitting K in stage1
-  // K steps in flight per wave (the bf16 operands are 4x the fp4 ones in registers)
-  static constexpr int PF1 = BM == 16 ? 7 : (ADT == DT_BF16 || NI == 64 ? 2 : 4);
+  // K steps in flight per wave (the bf16 operands are 4x the fp4 ones in registers; at 64
+  // columns fp8 keeps 2 (3: 272 -> 409 us at 1024 tokens), fp4 takes 3 (468 -> 447 us fused))
+  static constexpr int PF1 = BM == 16 ? 7 : (ADT == DT_FP4 && NI == 64 ? 3 : (ADT == DT_BF16 || NI == 64 ? 2 : 4));
   static constexpr int MINW1 = 2;                               // waves per SIMD kept
   // activation rows staged in LDS (fp8 measured faster with its rows in registers)
   static constexpr bool LDSA = BM == 16 && ADT != DT_FP8;
