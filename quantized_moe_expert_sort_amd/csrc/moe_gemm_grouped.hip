@@ -18,8 +18,11 @@
 // (or [4l, 4l+4)) after the wave's LDS address in m0), P steps in flight (P LDS buffers), one
 // barrier per step; Stage1 copies the e8m0 scales of a row 16 bytes (four K steps) at a time.  The copies are issued from inline assembly,
 // so the only waits on them are the explicit vmcnt waits of the pipeline.  The 16-byte chunks
-// of a row are stored XOR-swizzled (chunk p of row r at position p ^ swz(r)), so the 16 lanes
-// that read one chunk column of 16 rows for a matrix-core operand hit distinct LDS banks.
+// of an activation / intermediate row and of a Stage2 weight row are stored XOR-swizzled (chunk
+// p of row r at position p ^ swz(r)), so the 16 lanes that read one chunk column of 16 rows for
+// a matrix-core operand hit distinct LDS banks.  Stage1 weights arrive packed (moe_pack.hip):
+// one copy instruction moves a whole 1 KB block (16 rows x one K step, already in lane order),
+// so a lane group's operand read is 256 consecutive bytes.
 //
 // The grid is persistent: one workgroup per CU, each looping over work items.  Groups are
 // dealt to the 8 XCDs round robin (workgroup b runs on XCD b % 8) and the column blocks of a
