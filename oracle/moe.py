@@ -27,10 +27,13 @@ Precision: float64 accumulation and activation.  Where floating point decides a 
 requantization of the stage1 output), the value is first rounded to float32, the precision
 in which the GPU takes the same decision.
 
-Parity pins: see tests/test_oracle_moe.py -- SiTUv2 closed forms and limits, a brute-force
-sort via Python's sorted(), sort invariants and the decode padding statistic printed on
-PR 5118, a pure-Python per-token loop on tiny inputs, the dense-FFN special case against
-torch's linear algebra, and an exact small-integer GEMM case.
+Parity pins: see tests/test_oracle_moe.py -- SiTUv2 closed forms and limits; SiLU at points
+where the logistic function is rational (g = +-ln k), its odd and even parts, its limits, and
+as the large-beta limit of the pinned SiTUv2; relL2 against hand-computed values (normalised
+by the reference, every element counted); a brute-force sort via Python's sorted(), sort
+invariants and the decode padding statistic printed on PR 5118; a pure-Python per-token loop
+on tiny inputs; the dense-FFN special case against torch's linear algebra; and an exact
+small-integer GEMM case.  Every function here is pinned.
 """
 import numpy as np
 import scipy.special

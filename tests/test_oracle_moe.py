@@ -74,6 +74,79 @@ def test_situv2_bounds_zeros_and_saturation():
     assert np.all(om.situv2(big, 0.0 * big, BETA, LBETA) == 0)
 
 
+# ----------------------------------------------------------------------------- SiLU epilogue
+#
+# silu(g) * u (github ROCm/aiter PR 4471, "Motivation": the SiLU path stays next to SiTUv2).
+# Pinned by points where the logistic function is rational, by its symmetry, by its limits and
+# by the pinned SiTUv2, whose large-beta limit it is.
+
+def test_silu_rational_sigmoid_points():
+    # sigmoid(ln k) = k / (k + 1) and sigmoid(-ln k) = 1 / (k + 1)
+    for k in (3.0, 7.0, 0.25):
+        g = np.log(k)
+        for u in (1.0, -2.5, 40.0):
+            assert om.silu_mul(g, u) == pytest.approx(g * k / (k + 1) * u, rel=1e-15)
+            assert om.silu_mul(-g, u) == pytest.approx(-g / (k + 1) * u, rel=1e-15)
+
+
+def test_silu_odd_part_and_even_part():
+    # silu(g) - silu(-g) = g (sigmoid(g) + sigmoid(-g) = 1); silu(g) + silu(-g) = g tanh(g / 2)
+    g = np.linspace(-30, 30, 601)
+    one = np.ones_like(g)
+    assert np.allclose(om.silu_mul(g, one) - om.silu_mul(-g, one), g, rtol=1e-14, atol=1e-14)
+    assert np.allclose(om.silu_mul(g, one) + om.silu_mul(-g, one), g * np.tanh(g / 2), rtol=1e-12, atol=1e-14)
+
+
+def test_silu_limits_zero_and_linearity_in_up():
+    assert om.silu_mul(60.0, 3.0) == pytest.approx(180.0, rel=1e-15)      # g -> +inf: g * u
+    assert abs(om.silu_mul(-60.0, 3.0)) < 1e-20                            # g -> -inf: 0
+    assert om.silu_mul(0.0, 123.0) == 0.0 and om.silu_mul(1.7, 0.0) == 0.0
+    rng = np.random.default_rng(4)
+    g, u = rng.standard_normal(100) * 4, rng.standard_normal(100) * 4
+    assert np.allclose(om.silu_mul(g, 3 * u), 3 * om.silu_mul(g, u), rtol=1e-14, atol=0)
+
+
+def test_silu_is_the_large_beta_limit_of_situv2():
+    # the SiTUv2 pins above fix situv2; beta = linear_beta -> inf reduces it to silu(g) * u
+    # with a gap of order 1/beta^2
+    rng = np.random.default_rng(2)
+    g, u = rng.standard_normal(4000) * 3, rng.standard_normal(4000) * 3
+    errs = [np.max(np.abs(om.situv2(g, u, b, b) - om.silu_mul(g, u))) for b in (1e2, 1e3)]
+    assert errs[1] < 1e-2 and 90 < errs[0] / errs[1] < 110
+
+
+def test_activation_dispatch_selects_silu():
+    g, u = np.array([np.log(3.0)]), np.array([2.0])
+    assert om.activation(g, u, "silu")[0] == pytest.approx(np.log(3.0) * 0.75 * 2.0, rel=1e-15)
+
+
+# ----------------------------------------------------------------------------- relL2
+#
+# relL2 = ||got - ref||_2 / ||ref||_2 over every element (the parity measure of the tests).
+
+def test_rel_l2_hand_computed_values():
+    assert om.rel_l2([3.0, 4.0], [3.0, 4.0]) == 0.0
+    assert om.rel_l2([0.0, 0.0], [3.0, 4.0]) == 1.0                        # 5 / 5
+    assert om.rel_l2([6.0, 8.0], [3.0, 4.0]) == 1.0                        # 5 / 5: normalised by ref
+    assert om.rel_l2([3.0, 4.0], [6.0, 8.0]) == 0.5                        # 5 / 10
+    assert om.rel_l2([1.0, 2.0, 2.5], [1.0, 2.0, 2.0]) == pytest.approx(0.5 / 3.0, rel=1e-15)
+    # every element of a 2-D array counts: ||ref|| = 3, ||diff|| = 0.6
+    assert om.rel_l2([[1.0, 2.0], [2.0, 0.6]], [[1.0, 2.0], [2.0, 0.0]]) == pytest.approx(0.2, rel=1e-15)
+    # a zero reference: the norm of got itself
+    assert om.rel_l2([3.0, 4.0], [0.0, 0.0]) == 5.0
+
+
+def test_rel_l2_scale_invariance_and_float32_inputs():
+    rng = np.random.default_rng(8)
+    ref = rng.standard_normal(1000)
+    got = ref + 1e-3 * rng.standard_normal(1000)
+    r = om.rel_l2(got, ref)
+    assert om.rel_l2(1024.0 * got, 1024.0 * ref) == pytest.approx(r, rel=1e-14)
+    # float32 inputs are widened before the sums (no float32 accumulation)
+    assert om.rel_l2(got.astype(np.float32), ref.astype(np.float32)) == pytest.approx(
+        om.rel_l2(got.astype(np.float32).astype(np.float64), ref.astype(np.float32).astype(np.float64)), rel=0)
+
+
 def test_activation_rejects_unknown_and_missing_betas():
     with pytest.raises(ValueError):
         om.activation(np.zeros(2), np.zeros(2), "swiglu")
