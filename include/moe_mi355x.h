@@ -14,12 +14,15 @@
  *                    tanh evaluated as 2*sigmoid(2x)-1 (PR 4471 "Technical Details");
  *                    the intermediate re-encoded in the activation dtype; Stage2: MXFP4
  *                    down-projection, times the router weight, summed into each token's row.
- *   moe_pack_w1 reorders the Stage1 weights once into the layout moe_fused streams.
+ *   moe_pack_w1 reorders the Stage1 weights once into the layout moe_fused streams; moe_fused
+ *   takes a w1_layout tag and accepts only that packed layout.
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library never
- *     allocates or frees device memory and keeps no pointer after a call returns; it holds no
- *     mutable global state, so calls from several host threads are safe.
+ *     allocates or frees device memory and keeps no pointer after a call returns.  Its only
+ *     host-side state is the thread-local last HIP error (moe_last_hip_error), so calls from
+ *     several host threads are safe.  Launch shapes that depend on the device (the compute
+ *     unit count of the large-batch kernels) are queried for the current device at each call.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work on
  *     it and never synchronizes; results are ready when the stream reaches that point.
  *   - Arguments are validated on the host before anything is enqueued.  On a validation error
@@ -60,6 +63,12 @@ typedef enum { MOE_ACT_SITUV2 = 0, MOE_ACT_SILU = 1, MOE_ACT_NONE_TEST = 2 } moe
 /* Which stages moe_fused runs (see `stages` there). */
 typedef enum { MOE_STAGE_1 = 1, MOE_STAGE_2 = 2, MOE_STAGE_ALL = 3 } moe_stages_t;
 
+/* Byte layout of the Stage1 weights handed to moe_fused.  ROW_MAJOR is [E, 2I, D/2] fp4x2 as
+ * stored by a checkpoint; PACKED is what moe_pack_w1 writes from it.  moe_fused streams only
+ * PACKED (ROW_MAJOR -> MOE_ERR_UNSUPPORTED, any other value -> MOE_ERR_INVALID_ARG): the tag
+ * makes the caller state which bytes it passes, since both layouts have the same size. */
+typedef enum { MOE_W1_ROW_MAJOR = 0, MOE_W1_PACKED = 1 } moe_w1_layout_t;
+
 /* There are no default betas: PR 4463 "Three tuner defects" item 1 shows two sides silently
  * using different defaults.  beta and linear_beta must be finite and > 0 for SITUV2. */
 typedef struct {
@@ -81,8 +90,8 @@ typedef struct {
  * in these words (and sets them back to zero before it ends, so the layout can be reused
  * without sorting again).  Calls that use the same sync words must not overlap in time.
  * Word 0 is a sticky error flag: nonzero after a wait for another workgroup timed out (about
- * 0.25 s; the outputs of that call * are then invalid); only moe_sort clears it.  sync == NULL selects one launch per stage, which
- * measured faster on MI355X at every batch size tried (the single grid must hold Stage1's
+ * 0.25 s; the outputs of that call are then invalid); only moe_sort clears it.  sync == NULL
+ * selects one launch per stage, which measured faster on MI355X at every batch size tried (the single grid must hold Stage1's
  * register footprint, which lowers Stage2's occupancy); the single launch halves the number of
  * kernel launches per call, for callers bound by launch overhead. */
 typedef struct {
@@ -95,6 +104,13 @@ typedef struct {
   int32_t cap_tiles;         /* tiles the buffers hold, >= moe_cap_tiles(...) */
   int32_t block_m;           /* rows per tile: 16 or 32 */
 } moe_layout_t;
+
+/* Rows per tile the library's kernels are tuned for: 16 up to 512 tokens, 32 above (PR 5118
+ * "Summary" and "Optimizations Applied": block_m 16 for the decode batches, 32 for prefill;
+ * the crossover measured on MI355X with the packed weights lies between 512 and 768 tokens).
+ * Either value is accepted by every entry point; this is the default a caller should size its
+ * layout with. */
+static inline int32_t moe_block_m(int32_t tokens) { return tokens <= 512 ? 16 : 32; }
 
 /* Largest batch (exclusive) that moe_fused runs as one launch when layout->sync is given. */
 #define MOE_SINGLE_LAUNCH_MAX_TOKENS 2048
@@ -113,6 +129,9 @@ static inline int32_t moe_cap_tiles(int32_t tokens, int32_t topk, int32_t num_lo
   int64_t e = num_local_experts < n ? num_local_experts : n;
   return (int32_t)((n + block_m - 1) / block_m + e);
 }
+
+/* Most local experts moe_sort handles. */
+#define MOE_SORT_MAX_EXPERTS 2048
 
 /* Routed rows are counted in chunks of this many flat indices. */
 #define MOE_SORT_CHUNK 4096
@@ -169,7 +188,9 @@ static inline size_t moe_fused_ws_bytes(int32_t tokens, int32_t model_dim, int32
  *             be NULL here; moe_fused needs it; sync, when given, is set to zero).
  *   ws        device scratch of ws_bytes >= moe_sort_ws_bytes(tokens, topk, num_local_experts).
  * The result is unique and bit-exact: it does not depend on launch order or timing.
- * Limits: 1 <= tokens*topk < 2^31, 1 <= num_local_experts <= 8192. */
+ * Limits: tokens*topk < 2^31 (tokens == 0 writes an empty layout), 1 <= num_local_experts <= 2048
+ * (MOE_SORT_MAX_EXPERTS: the per-expert counters live in LDS); larger values ->
+ * MOE_ERR_UNSUPPORTED. */
 moe_status_t moe_sort(const int32_t *topk_ids, const float *topk_w, int32_t tokens, int32_t topk,
                       int32_t expert_begin, int32_t num_local_experts, const moe_layout_t *layout,
                       void *ws, size_t ws_bytes, void *stream);
@@ -188,9 +209,13 @@ moe_status_t moe_quant_act(const uint16_t *x_bf16, int64_t rows, int64_t cols, i
                            void *q_out, uint8_t *scale_out, void *stream);
 
 /* moe_pack_w1 -- reorder the Stage1 weights once into the layout moe_fused reads (a one-time
- * weight preparation, as the pages' kernels read pre-shuffled weights: PR 5118 "Summary").
+ * weight preparation, not a step of the pages' operator).  A matrix-core operand of 16 weight
+ * rows at one 128-deep K step is then 1 KB of consecutive bytes in lane order instead of 16
+ * separate 64-byte pieces; on MI355X this made Stage1 12-18% faster from 1 to 1024 tokens
+ * (per-tile Stage1 9.1 -> 8.0 us at 1 token, 339 -> 278 us at 1024 tokens).
  *   w1         [E, 2I, D/2] fp4x2, row-major (rows 0..I-1 gate, I..2I-1 up).
- *   w1_packed  E*2I*D/2 bytes, caller-owned, not aliasing w1: 1 KB blocks (e, f, s) for row
+ *   w1_packed  E*2I*D/2 bytes, caller-owned; the byte ranges of w1 and w1_packed must not
+ *              overlap (else MOE_ERR_INVALID_ARG): 1 KB blocks (e, f, s) for row
  *              group f < 2I/16 and K step s < D/128, in that order (s fastest); byte
  *              16*(16*g + r) + b of a block is byte 64*s + 16*g + b of row 16*f + r of expert e
  *              (g < 4, r < 16, b < 16).  The e8m0 scales keep their layout.
@@ -205,6 +230,8 @@ moe_status_t moe_pack_w1(const uint8_t *w1, int32_t num_experts, int32_t model_d
  *   x_scale   [tokens, D/32] e8m0 for FP8 / FP4; must be NULL for BF16.
  *   w1        Stage1 weights [E, 2I, D/2] fp4x2 (rows 0..I-1 gate, I..2I-1 up) in the packed
  *             layout moe_pack_w1 writes.
+ *   w1_layout MOE_W1_PACKED (the only layout moe_fused reads; MOE_W1_ROW_MAJOR ->
+ *             MOE_ERR_UNSUPPORTED: pack it once with moe_pack_w1 first).
  *   w1_scale  [E, 2I, D/32] e8m0, row-major.
  *   w2, w2_scale  [E, D, I/2] fp4x2 and [E, D, I/32] e8m0.
  *   topk_w    [tokens, topk] fp32 router weights; row v of the layout is scaled by topk_w[v].
@@ -225,7 +252,7 @@ moe_status_t moe_pack_w1(const uint8_t *w1, int32_t num_experts, int32_t model_d
  * rows in ascending k in fp32 and rounds to bf16: the result is deterministic, and the single-launch and per-stage paths give the same
  * bits.  layout->row_of must be set. */
 moe_status_t moe_fused(const void *x, const uint8_t *x_scale, int32_t a_dtype,
-                       const uint8_t *w1, const uint8_t *w1_scale,
+                       const uint8_t *w1, int32_t w1_layout, const uint8_t *w1_scale,
                        const uint8_t *w2, const uint8_t *w2_scale,
                        const float *topk_w, const moe_layout_t *layout,
                        int32_t tokens, int32_t topk, int32_t num_local_experts,

@@ -13,6 +13,7 @@ import torch
 DT_BF16, DT_FP8, DT_FP4 = 0, 1, 2
 ACT_SITUV2, ACT_SILU, ACT_NONE_TEST = 0, 1, 2
 STAGE_1, STAGE_2, STAGE_ALL = 1, 2, 3
+W1_ROW_MAJOR, W1_PACKED = 0, 1
 DTYPES = {"bf16": DT_BF16, "fp8": DT_FP8, "fp4": DT_FP4}
 ACTS = {"situv2": ACT_SITUV2, "silu": ACT_SILU, "none_test": ACT_NONE_TEST}
 
@@ -59,8 +60,8 @@ def lib():
         L.moe_sort.restype = i32
         L.moe_quant_act.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         L.moe_quant_act.restype = i32
-        L.moe_fused.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(Layout), i32, i32, i32,
-                                i32, i32, ctypes.POINTER(ActParams), vp, vp, sz, i32, vp]
+        L.moe_fused.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp, ctypes.POINTER(Layout), i32, i32,
+                                i32, i32, i32, ctypes.POINTER(ActParams), vp, vp, sz, i32, vp]
         L.moe_fused.restype = i32
         L.moe_pack_w1.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_pack_w1.restype = i32
@@ -88,6 +89,11 @@ def _stream():
 
 def _align256(b):
     return (b + 255) & ~255
+
+
+def block_m(tokens):
+    """Rows per tile the kernels are tuned for (moe_block_m of the header)."""
+    return 16 if tokens <= 512 else 32
 
 
 def cap_tiles(tokens, topk, num_local_experts, block_m):
@@ -203,9 +209,11 @@ def moe_quant_act(x_bf16, dt, q=None, scale=None):
 
 
 def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, num_local_experts,
-              act="situv2", beta=None, linear_beta=None, out=None, ws=None, stages=STAGE_ALL):
-    """Stage1 + Stage2 over a layout from moe_sort (w1 packed by moe_pack_w1); returns out [T, D] bf16 (or, for
-    act="none_test", the workspace tensor holding the raw gate/up sums).  stages selects
+              act="situv2", beta=None, linear_beta=None, out=None, ws=None, stages=STAGE_ALL,
+              w1_layout=W1_PACKED):
+    """Stage1 + Stage2 over a layout from moe_sort; returns out [T, D] bf16 (or, for
+    act="none_test", the workspace tensor holding the raw gate/up sums).  w1 is in the layout
+    named by w1_layout (the library reads W1_PACKED, as moe_pack_w1 writes it).  stages selects
     STAGE_1, STAGE_2 (reusing the intermediate a STAGE_1 call left in the same ws) or both."""
     d = DTYPES[a_dtype] if isinstance(a_dtype, str) else a_dtype
     a = ACTS[act] if isinstance(act, str) else act
@@ -220,7 +228,7 @@ def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, n
                          device=topk_w.device)
     if out is None and a != ACT_NONE_TEST:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=topk_w.device)
-    _check("moe_fused", lib().moe_fused(_ptr(x), _ptr(x_scale), d, _ptr(w1), _ptr(w1_scale), _ptr(w2),
+    _check("moe_fused", lib().moe_fused(_ptr(x), _ptr(x_scale), d, _ptr(w1), w1_layout, _ptr(w1_scale), _ptr(w2),
                                         _ptr(w2_scale), _ptr(topk_w), ctypes.byref(layout.c), T, K,
                                         num_local_experts, D, I, ctypes.byref(params), _ptr(out),
                                         _ptr(ws), ws.numel(), stages, _stream()))

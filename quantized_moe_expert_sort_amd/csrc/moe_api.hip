@@ -55,10 +55,14 @@ moe_status_t moe_sort(const int32_t* topk_ids, const float* topk_w, int32_t toke
 
 moe_status_t moe_pack_w1(const uint8_t* w1, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
                          uint8_t* w1_packed, void* stream) {
-  if (!w1 || !w1_packed || w1 == w1_packed) return MOE_ERR_INVALID_ARG;
+  if (!w1 || !w1_packed) return MOE_ERR_INVALID_ARG;
   if (num_experts < 1 || model_dim <= 0 || inter_dim <= 0) return MOE_ERR_INVALID_ARG;
   if (model_dim % 128 != 0 || inter_dim % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)num_experts * 2 * inter_dim * (model_dim / 2) / 16 >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  // the copy reads w1 and writes w1_packed in a different order: the two ranges must be disjoint
+  const uintptr_t bytes = (uintptr_t)num_experts * 2 * (uintptr_t)inter_dim * (uintptr_t)(model_dim / 2);
+  const uintptr_t a = (uintptr_t)w1, b = (uintptr_t)w1_packed;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_pack_w1(w1, w1_packed, num_experts, model_dim, inter_dim, (hipStream_t)stream));
 }
 
@@ -72,12 +76,14 @@ moe_status_t moe_quant_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, i
 }
 
 moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
-                       const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                       int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
                        const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
                        int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
                        const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
                        int32_t stages, void* stream) {
   if (!valid_dtype(a_dtype)) return MOE_ERR_INVALID_ARG;
+  if (w1_layout != MOE_W1_PACKED && w1_layout != MOE_W1_ROW_MAJOR) return MOE_ERR_INVALID_ARG;
+  if (w1_layout != MOE_W1_PACKED) return MOE_ERR_UNSUPPORTED;   // the kernels stream packed blocks only
   if (stages != MOE_STAGE_1 && stages != MOE_STAGE_2 && stages != MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
   if (!act) return MOE_ERR_INVALID_ARG;
   if (act->act != MOE_ACT_SITUV2 && act->act != MOE_ACT_SILU && act->act != MOE_ACT_NONE_TEST)

@@ -19,7 +19,7 @@ struct SortLayout {
   int64_t cap_tiles;
 };
 
-constexpr int MAX_SORT_EXPERTS = 2048;
+constexpr int MAX_SORT_EXPERTS = MOE_SORT_MAX_EXPERTS;
 
 hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, int expert_begin,
                        int E, int block_m, const SortLayout& L, void* ws, hipStream_t s);

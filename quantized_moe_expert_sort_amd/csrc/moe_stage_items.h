@@ -4,12 +4,13 @@
 //
 // Stage1 item (tile, nb) (github ROCm/aiter PR 6259 "Technical Details": SiTUv2 in the stage1
 //   epilogue): block_m sorted rows x NI intermediate columns.  The gate columns [n0, n0+NI)
-//   and the matching up columns [I+n0, I+n0+NI) are computed together (NI = 8 puts both in one
-//   16-column matrix-core fragment), and g and u of one output element meet in the LDS
-//   reduction.  KW waves split the K = model_dim reduction into contiguous
-//   ranges of 128-deep steps; each lane streams its weight bytes and its gathered activation row
-//   straight from memory into matrix-core operands (every byte is loaded once per item), issuing
-//   the loads of PF steps before the first MFMA that uses them; the partial sums meet in LDS.
+//   and the matching up columns [I+n0, I+n0+NI) are computed together (NI a multiple of 16, so
+//   every 16-row weight fragment is one packed block of gate or of up rows), and g and u of one
+//   output element meet in the LDS reduction.  KW waves split the K = model_dim reduction into
+//   contiguous ranges of 128-deep steps; each lane streams its weight bytes and its gathered
+//   activation row straight from memory into matrix-core operands (every byte is loaded once
+//   per item), issuing the loads of PF steps before the first MFMA that uses them; the partial
+//   sums meet in LDS.
 //   The epilogue applies SiTUv2 or SiLU and re-encodes the intermediate: bf16, or fp8 / fp4 with
 //   one e8m0 scale per 32 columns (the 32 columns of a block are 32 lanes of one wave).
 // Stage2 item (tile, nb) (PR 5118 review items 9-10: bf16 x MXFP4 stage2 with a per-token
@@ -79,7 +80,9 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
   constexpr int NT = KW * WAVE;
   constexpr int MF = BM / 16;
   constexpr int NB = 2 * NI / 16;
-  static_assert(NI % 8 == 0, "gate and up columns fill whole 16-column fragments");
+  // the packed-w1 addressing below takes fragment j's 16 weight rows as one packed block
+  // (row n of the block at n % 16 == r16): the gate and the up rows of a fragment never mix
+  static_assert(NI % 16 == 0, "gate and up columns fill whole 16-row packed blocks");
   static_assert((BM * NI) % NT == 0 || (BM * NI) % WAVE == 0 && BM * NI < NT,
                 "every wave of the epilogue runs the same trip count on all of its lanes");
   static_assert(ADT == DT_BF16 || NI % 32 == 0, "a quantized intermediate needs whole 32-column blocks");

@@ -33,6 +33,17 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_block_m_rule_matches_header_and_inputs():
+    from quantized_moe_expert_sort_amd import inputs as gen
+    src = open(HEADER).read()
+    m = re.search(r"moe_block_m\(int32_t tokens\) \{ return tokens <= (\d+) \? (\d+) : (\d+); \}", src)
+    lim, small, large = (int(v) for v in m.groups())
+    for t in (1, 4, 16, 64, 256, 511, 512, 513, 1024, 8192, 16384):
+        want = small if t <= lim else large
+        assert qm.block_m(t) == want
+        assert gen.Workload("w", t, 8, 2, 256, 128, "bf16").block_m == want
+
+
 def test_header_size_helpers_match_binding():
     # the binding mirrors the header's static inline size helpers; spot-check the formulas
     assert qm.cap_tiles(1, 16, 896, 16) == 17
@@ -79,10 +90,10 @@ def test_sort_validation():
 
 
 def _fused(a_dtype=0, xs=None, act=0, beta=4.0, lb=25.0, T=4, K=2, E=8, D=256, I=128, layout=None,
-           ws_bytes=1 << 30, out=P, x=P, stages=3):
+           ws_bytes=1 << 30, out=P, x=P, stages=3, w1_layout=1):
     lay = _layout(cap=qm.cap_tiles(T, K, E, 16)) if layout is None else layout
     ap = qm.ActParams(act, beta, lb)
-    return qm.lib().moe_fused(x, xs, a_dtype, P, P, P, P, P, ctypes.byref(lay), T, K, E, D, I,
+    return qm.lib().moe_fused(x, xs, a_dtype, P, w1_layout, P, P, P, P, ctypes.byref(lay), T, K, E, D, I,
                               ctypes.byref(ap), out, P, ws_bytes, stages, None)
 
 
@@ -104,6 +115,9 @@ def test_fused_validation():
     assert _fused(layout=_layout(cap=100, row_of=False)) == INVALID   # the combine needs row_of
     assert _fused(stages=0) == INVALID
     assert _fused(stages=4) == INVALID
+    assert _fused(w1_layout=0) == UNSUPPORTED           # row-major w1: pack it with moe_pack_w1 first
+    assert _fused(w1_layout=2) == INVALID
+    assert _fused(w1_layout=0, T=0) == UNSUPPORTED      # the tag is checked before anything else
     assert _fused(T=0) == OK                            # empty batch: nothing to do
 
 
@@ -122,6 +136,9 @@ def test_pack_validation():
     f = qm.lib().moe_pack_w1
     P2 = ctypes.c_void_p(8192)
     assert f(P, 2, 256, 128, P, None) == INVALID        # in place
+    n = 2 * 2 * 128 * 128                               # bytes of w1 at E=2, D=256, I=128
+    assert f(P, 2, 256, 128, ctypes.c_void_p(P.value + n - 16), None) == INVALID   # overlap at the end
+    assert f(ctypes.c_void_p(P.value + 16), 2, 256, 128, P, None) == INVALID       # overlap at the start
     assert f(None, 2, 256, 128, P2, None) == INVALID
     assert f(P, 0, 256, 128, P2, None) == INVALID       # no experts
     assert f(P, 2, 192, 128, P2, None) == UNSUPPORTED   # model_dim % 128
