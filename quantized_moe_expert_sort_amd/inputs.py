@@ -63,7 +63,10 @@ WORKLOADS = {
     "ep-8192": Workload("ep-8192", 8192, 112, 16, 3584, 3072, "fp8", global_experts=896),
     "pre-16384": Workload("pre-16384", 16384, 896, 16, 3584, 384, "fp4", zipf_s=1.1),
     # the pages' own large-batch timing shape (uniform routing over all 896 experts)
+    "pre-a16-2048": Workload("pre-a16-2048", 2048, 896, 16, 3584, 384, "bf16"),
+    "pre-a16-4096": Workload("pre-a16-4096", 4096, 896, 16, 3584, 384, "bf16"),
     "pre-a16-8192": Workload("pre-a16-8192", 8192, 896, 16, 3584, 384, "bf16"),
+    "pre-a16-16384": Workload("pre-a16-16384", 16384, 896, 16, 3584, 384, "bf16"),
     "pre-a8-8192": Workload("pre-a8-8192", 8192, 896, 16, 3584, 384, "fp8"),
 }
 

@@ -1,7 +1,8 @@
 """The single-launch path of moe_fused (a layout with sync words, batches below
 SINGLE_LAUNCH_MAX_TOKENS; opt-in) against the default per-stage launches on the same inputs: the
-same output bits, since both run the same Stage1 / Stage2 / combine arithmetic.  Also: the sort zeroes the
-sync words, every call leaves them zero (so a layout can be reused), and no wait timed out."""
+same output bits, since both run the same Stage1 / Stage2 / combine arithmetic, and every token's
+output row within the bar against the oracle.  Also: the sort zeroes the sync words, every call
+leaves them zero (so a layout can be reused), and no wait timed out."""
 import numpy as np
 import pytest
 import torch
@@ -9,6 +10,7 @@ import torch
 import quantized_moe_expert_sort_amd as qm
 from oracle import moe as om
 from quantized_moe_expert_sort_amd import inputs as gen
+from _parity import RequantExplainer, assert_rows_close
 
 pytestmark = pytest.mark.gpu
 BETA, LBETA = gen.BETA, gen.LINEAR_BETA
@@ -71,16 +73,23 @@ def test_single_launch_matches_per_stage_bits(T, Er, K, D, I, eb, E, bm, a_dtype
     assert torch.equal(out_s.view(torch.int16), out_m.view(torch.int16))
     # every counter was set back to zero by its last user
     assert int(torch.count_nonzero(lay_s.sync).item()) == 0
-    # and the outputs are the operator's (oracle on a few tokens)
+    # and the outputs are the operator's: every token's row against the oracle
     ids = pb["ids"]
-    local = np.nonzero(((ids >= eb) & (ids < eb + E)).any(axis=1))[0]
-    toks = sorted({int(local[0]), int(local[-1])}) if len(local) else []
+    local = ((ids >= eb) & (ids < eb + E)).any(axis=1)
     got = out_s.float().cpu().numpy().astype(np.float64)
-    if toks:
-        ref = om.moe_tokens(toks, pb["x"], a_dtype, *pb["host_w"], ids, pb["w"], eb, E, act, BETA, LBETA)
-        assert om.rel_l2(got[toks], ref) <= (5e-3 if a_dtype == "bf16" else 2e-2)
-    nonlocal_ = ~((ids >= eb) & (ids < eb + E)).any(axis=1)
-    assert np.all(got[nonlocal_] == 0)
+    ref, inter = om.moe_fused(pb["x"], a_dtype, *pb["host_w"], ids, pb["w"], eb, E, act, BETA, LBETA,
+                              return_intermediate=True)
+    tol = 5e-3 if a_dtype == "bf16" else 2e-2
+    ex = None
+    if a_dtype != "bf16":
+        # the per-stage call's workspace holds its intermediate (the same bits as the single launch)
+        ws = torch.empty(qm.fused_ws_bytes(T, D, I, lay_m.cap, bm, qm.DTYPES[a_dtype], qm.ACTS[act]),
+                         dtype=torch.uint8, device="cuda")
+        qm.moe_fused(pb["xa"], pb["xs"], a_dtype, *pb["wd"], pb["w_d"], lay_m, E, act, BETA, LBETA, ws=ws)
+        torch.cuda.synchronize()
+        ex = RequantExplainer(got, ws.cpu().numpy(), lay_m.row_of.cpu().numpy(), inter, None, a_dtype, act, BETA,
+                              LBETA, pb["host_w"][2], pb["host_w"][3], ids, pb["w"], eb, D, I, lay_m.cap * bm, tol)
+    assert_rows_close(got, ref, local, tol, f"{a_dtype} {act}", explain=ex)
 
 
 def test_single_launch_reuses_layout_without_sorting_again():
