@@ -18,11 +18,12 @@
  *   takes a w1_layout tag and accepts only that packed layout.
  *
  * Conventions for every entry point
- *   - All tensor pointers are DEVICE pointers owned by the caller.  The library never
- *     allocates or frees device memory and keeps no pointer after a call returns.  Its only
- *     host-side state is the thread-local last HIP error (moe_last_hip_error), so calls from
- *     several host threads are safe.  Launch shapes that depend on the device (the compute
- *     unit count of the large-batch kernels) are queried for the current device at each call.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  No call allocates or frees
+ *     device memory, and none keeps a caller's pointer after it returns.  Host-side state: the
+ *     thread-local last HIP error (moe_last_hip_error) and, for moe_fused_noalloc only, the
+ *     device address of its fixed scratch array on each device (taken once, under a lock), so
+ *     calls from several host threads are safe.  Launch shapes that depend on the device (the
+ *     compute unit count of the large-batch kernels) are queried at each call.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work on
  *     it and never synchronizes; results are ready when the stream reaches that point.
  *   - Arguments are validated on the host before anything is enqueued.  On a validation error
@@ -259,6 +260,33 @@ moe_status_t moe_fused(const void *x, const uint8_t *x_scale, int32_t a_dtype,
                        int32_t model_dim, int32_t inter_dim, const moe_act_params_t *act,
                        uint16_t *out_bf16, void *ws, size_t ws_bytes, int32_t stages,
                        void *stream);
+
+/* Bytes of the fixed device scratch moe_fused_noalloc works in (128 MiB per device). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* moe_fused_noalloc -- moe_fused for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments,
+ * kernels and results as moe_fused, without ws / ws_bytes.  Its workspace is a scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on, from the first
+ * call on that device until the process ends; the call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).
+ *   - A call whose moe_fused_ws_bytes(...) exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ *     MOE_ERR_WORKSPACE before anything is launched (at model_dim 3584 and inter_dim 384 the
+ *     scratch holds batches up to 128 tokens of any activation dtype at top-16 over 896 experts;
+ *     use moe_fused with a caller workspace above that).
+ *   - Every call on a device shares that device's scratch, which keeps the last call's
+ *     contents: calls that overlap in time on one device (other streams or other threads) race,
+ *     and a MOE_STAGE_2 call reads the intermediate the last MOE_STAGE_1 call on that device left.
+ *     No part of the scratch needs to start at zero: a call writes every byte it reads there.
+ *   - The first call on a device takes the scratch's device address (hipGetSymbolAddress, not an
+ *     allocation); a failure there returns MOE_ERR_HIP. */
+moe_status_t moe_fused_noalloc(const void *x, const uint8_t *x_scale, int32_t a_dtype,
+                               const uint8_t *w1, int32_t w1_layout, const uint8_t *w1_scale,
+                               const uint8_t *w2, const uint8_t *w2_scale,
+                               const float *topk_w, const moe_layout_t *layout,
+                               int32_t tokens, int32_t topk, int32_t num_local_experts,
+                               int32_t model_dim, int32_t inter_dim, const moe_act_params_t *act,
+                               uint16_t *out_bf16, int32_t stages, void *stream);
 
 /* The hipError_t value behind the last MOE_ERR_HIP returned on this thread (0 if none). */
 int32_t moe_last_hip_error(void);

@@ -22,7 +22,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
 SORT_CHUNK = 4096
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
-EXPORTS = ("moe_sort", "moe_quant_act", "moe_pack_w1", "moe_fused", "moe_last_hip_error")
+EXPORTS = ("moe_sort", "moe_quant_act", "moe_pack_w1", "moe_fused", "moe_fused_noalloc", "moe_last_hip_error")
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class MoeError(RuntimeError):
@@ -63,6 +64,9 @@ def lib():
         L.moe_fused.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp, ctypes.POINTER(Layout), i32, i32,
                                 i32, i32, i32, ctypes.POINTER(ActParams), vp, vp, sz, i32, vp]
         L.moe_fused.restype = i32
+        L.moe_fused_noalloc.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp, ctypes.POINTER(Layout), i32, i32,
+                                        i32, i32, i32, ctypes.POINTER(ActParams), vp, i32, vp]
+        L.moe_fused_noalloc.restype = i32
         L.moe_pack_w1.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_pack_w1.restype = i32
         L.moe_last_hip_error.argtypes = []
@@ -233,3 +237,25 @@ def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, n
                                         num_local_experts, D, I, ctypes.byref(params), _ptr(out),
                                         _ptr(ws), ws.numel(), stages, _stream()))
     return ws if a == ACT_NONE_TEST else out
+
+
+def moe_fused_noalloc(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, num_local_experts,
+                      act="situv2", beta=None, linear_beta=None, out=None, stages=STAGE_ALL,
+                      w1_layout=W1_PACKED):
+    """moe_fused with the library's fixed per-device scratch as its workspace (nothing allocated
+    for the workspace; calls on one device share it and must not overlap).  Returns out."""
+    d = DTYPES[a_dtype] if isinstance(a_dtype, str) else a_dtype
+    a = ACTS[act] if isinstance(act, str) else act
+    T, K = topk_w.shape
+    D = w2.shape[1]
+    I = w2.shape[2] * 2
+    if a == ACT_SITUV2 and (beta is None or linear_beta is None):
+        raise ValueError("SiTUv2 needs beta and linear_beta (there are no defaults)")
+    params = ActParams(a, 0.0 if beta is None else beta, 0.0 if linear_beta is None else linear_beta)
+    if out is None and a != ACT_NONE_TEST:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=topk_w.device)
+    _check("moe_fused_noalloc", lib().moe_fused_noalloc(_ptr(x), _ptr(x_scale), d, _ptr(w1), w1_layout,
+                                                        _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(topk_w),
+                                                        ctypes.byref(layout.c), T, K, num_local_experts, D, I,
+                                                        ctypes.byref(params), _ptr(out), stages, _stream()))
+    return out

@@ -1,11 +1,46 @@
 // extern "C" entry points of libmoe_mi355x.so: argument validation on the host, then the
-// kernel launchers.  Nothing here allocates, synchronizes or keeps state between calls except
-// the thread-local copy of the last HIP error.
+// kernel launchers.  Nothing here allocates or synchronizes.  State kept between calls: the
+// thread-local copy of the last HIP error, and for moe_fused_noalloc the per-device address of
+// the library's fixed scratch array (taken once per device).
 #include <cmath>
+#include <mutex>
 
 #include "moe_kernels.h"
 
+// Workspace of moe_fused_noalloc, for callers that cannot allocate: one copy per device, held
+// until the process ends, shared by every call on that device.  In host code this name is only
+// a stand-in for the symbol; kernels get the device address noalloc_scratch() takes for the
+// current device with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array (taken once per device, with that
+// device current).  On failure returns null and sets *err.
+void* noalloc_scratch(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !p) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 thread_local int32_t g_last_hip_error = 0;
 
@@ -75,12 +110,18 @@ moe_status_t moe_quant_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, i
   return hip_status(moe::launch_quant_act(x_bf16, rows, cols, dt, q_out, scale_out, (hipStream_t)stream));
 }
 
-moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
-                       int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
-                       const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
-                       int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
-                       const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
-                       int32_t stages, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_fused and moe_fused_noalloc: the same validation and launches; the no-alloc variant takes
+// its workspace from the scratch array (scratch == true; ws and ws_bytes are ignored).
+moe_status_t fused_call(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
+                        int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                        const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
+                        int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
+                        const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
+                        int32_t stages, void* stream, bool use_scratch) {
   if (!valid_dtype(a_dtype)) return MOE_ERR_INVALID_ARG;
   if (w1_layout != MOE_W1_PACKED && w1_layout != MOE_W1_ROW_MAJOR) return MOE_ERR_INVALID_ARG;
   if (w1_layout != MOE_W1_PACKED) return MOE_ERR_UNSUPPORTED;   // the kernels stream packed blocks only
@@ -100,13 +141,20 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
   if (st != MOE_OK) return st;
   if ((int64_t)layout->cap_tiles * layout->block_m >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   if (tokens == 0) return MOE_OK;
-  if (!x || !w1 || !w1_scale || !w2 || !w2_scale || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (!x || !w1 || !w1_scale || !w2 || !w2_scale || !topk_w || (!use_scratch && !ws)) return MOE_ERR_INVALID_ARG;
   if ((a_dtype == MOE_DT_BF16) != (x_scale == nullptr)) return MOE_ERR_INVALID_ARG;
   if (act->act != MOE_ACT_NONE_TEST && (stages & MOE_STAGE_2) && (!out_bf16 || !layout->row_of))
     return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < moe_fused_ws_bytes(tokens, model_dim, inter_dim, layout->cap_tiles, layout->block_m,
-                                    a_dtype, act->act))
-    return MOE_ERR_WORKSPACE;
+  const size_t need = moe_fused_ws_bytes(tokens, model_dim, inter_dim, layout->cap_tiles, layout->block_m,
+                                         a_dtype, act->act);
+  if (use_scratch) {
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    hipError_t err = hipSuccess;
+    ws = noalloc_scratch(&err);
+    if (!ws) return hip_status(err);
+    ws_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+  }
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
 
   const size_t rows = (size_t)layout->cap_tiles * layout->block_m;
   uint8_t* base = (uint8_t*)ws;
@@ -152,6 +200,30 @@ moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, c
       act->act != MOE_ACT_NONE_TEST)
     return hip_status(moe::launch_single(a, (hipStream_t)stream));
   return hip_status(moe::launch_fused(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
+                       int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                       const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
+                       int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
+                       const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
+                       int32_t stages, void* stream) {
+  return fused_call(x, x_scale, a_dtype, w1, w1_layout, w1_scale, w2, w2_scale, topk_w, layout, tokens, topk,
+                    num_local_experts, model_dim, inter_dim, act, out_bf16, ws, ws_bytes, stages, stream, false);
+}
+
+moe_status_t moe_fused_noalloc(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
+                               int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2,
+                               const uint8_t* w2_scale, const float* topk_w, const moe_layout_t* layout,
+                               int32_t tokens, int32_t topk, int32_t num_local_experts, int32_t model_dim,
+                               int32_t inter_dim, const moe_act_params_t* act, uint16_t* out_bf16,
+                               int32_t stages, void* stream) {
+  return fused_call(x, x_scale, a_dtype, w1, w1_layout, w1_scale, w2, w2_scale, topk_w, layout, tokens, topk,
+                    num_local_experts, model_dim, inter_dim, act, out_bf16, nullptr, 0, stages, stream, true);
 }
 
 }  // extern "C"

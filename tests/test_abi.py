@@ -122,6 +122,34 @@ def test_fused_validation():
 
 
 @no_gpu
+def test_fused_noalloc_validation():
+    f = qm.lib().moe_fused_noalloc
+
+    def call(a_dtype=0, xs=None, T=4, K=2, E=8, D=256, I=128, cap=None, bm=16, w1_layout=1, act=0):
+        lay = _layout(cap=qm.cap_tiles(T, K, E, bm) if cap is None else cap, bm=bm)
+        ap = qm.ActParams(act, 4.0, 25.0)
+        return f(P, xs, a_dtype, P, w1_layout, P, P, P, P, ctypes.byref(lay), T, K, E, D, I, ctypes.byref(ap), P,
+                 3, None)
+    assert call(a_dtype=7) == INVALID
+    assert call(w1_layout=0) == UNSUPPORTED
+    assert call(act=9) == UNSUPPORTED
+    assert call(D=200) == UNSUPPORTED
+    assert call(cap=1) == CAPACITY
+    assert call(T=0) == OK
+    # more than the fixed scratch: rejected on the host before the scratch is looked up
+    T = 1024
+    need = qm.fused_ws_bytes(T, 3584, 384, qm.cap_tiles(T, 16, 896, 32), 32, 1, 0)
+    assert need > qm.NOALLOC_SCRATCH_BYTES
+    assert call(a_dtype=1, xs=P, T=T, K=16, E=896, D=3584, I=384, bm=32) == WORKSPACE
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert int(m.group(1)) << int(m.group(2)) == qm.NOALLOC_SCRATCH_BYTES
+
+
+@no_gpu
 def test_quant_validation():
     q = qm.lib().moe_quant_act
     assert q(P, 4, 64, 0, P, P, None) == INVALID       # bf16 is not a quantized format
