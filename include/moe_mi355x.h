@@ -155,28 +155,61 @@ static inline size_t moe_row_bytes(int32_t cols, int32_t dt) {
 /* Bytes per element of the per-row Stage2 outputs (bf16 for every activation dtype). */
 static inline size_t moe_rowout_elem_bytes(int32_t a_dtype) { (void)a_dtype; return 2; }
 
-/* Workspace of moe_fused, in this order (each part 256-byte aligned): the per-row Stage2 outputs
- * [cap*bm, D] (bf16; router weight applied on the per-tile path, see moe_rowout_elem_bytes), the stage1
- * intermediate [cap*bm, I] in a_dtype plus its [cap*bm, I/32] e8m0 scales (fp8/fp4), a
- * [cap] list of tile groups plus its count (large batches), and for NONE_TEST a fp32
- * [cap*bm, 2I] debug area holding the raw gate (cols 0..I-1) and up (I..2I-1) sums of each
- * layout row. */
+/* Most experts the large-batch Stage2 takes token-major (see moe_fused: experts with at least a
+ * quarter of the tokens' rows). */
+#define MOE_HOT_MAX 16
+
+/* Workspace of moe_fused: byte offsets of its parts (each 256-byte aligned) and the total.
+ *   rowout    [cap*bm, D] bf16 per-row Stage2 outputs (router weight applied on the per-tile
+ *             path, by the combine after the large-batch Stage2);
+ *   inter     [cap*bm + 1, I] Stage1 intermediate in a_dtype (codes), in layout-row order; the
+ *             extra last row is a zero row the token-major Stage2 reads for absent (token, expert)
+ *             pairs;  iscale: its [cap*bm + 1, I/32] e8m0 scales (fp8 / fp4);
+ *   groups    [cap] (first tile, tile count) groups of one expert's tiles, then their count;
+ *   cgroups   the same list without the token-major (hot) experts' groups, then its count;
+ *   tile_hot  [cap] hot index of each tile's expert or -1;  hot_e: [MOE_HOT_MAX] hot experts and
+ *             their count;
+ *   hotpos, hotw [T, MOE_HOT_MAX] each token's layout row and router weight per hot expert;
+ *   hotmask   [T] the token's slots k whose expert is hot (bit k);
+ *   hot_out   [T, D] bf16 sum over the token's hot experts of the router-weighted Stage2 rows;
+ *   dbg       (NONE_TEST only) fp32 [cap*bm, 2I] raw gate (cols 0..I-1) and up (I..2I-1) sums of
+ *             each layout row. */
+typedef struct {
+  size_t rowout, inter, iscale, groups, cgroups, tile_hot, hot_e, hotpos, hotw, hotmask, hot_out, dbg, total;
+} moe_fused_ws_parts_t;
+
+static inline moe_fused_ws_parts_t moe_fused_ws_parts(int32_t tokens, int32_t model_dim, int32_t inter_dim,
+                                                      int32_t cap_tiles, int32_t block_m, int32_t a_dtype,
+                                                      int32_t act) {
+  moe_fused_ws_parts_t w;
+  size_t rows = (size_t)cap_tiles * block_m, o = 0;
+  size_t t = tokens > 0 ? (size_t)tokens : 0;
+  w.rowout = o;   o += moe_align256(rows * (size_t)model_dim * moe_rowout_elem_bytes(a_dtype));
+  w.inter = o;    o += moe_align256((rows + 1) * moe_row_bytes(inter_dim, a_dtype));
+  w.iscale = o;   o += moe_align256(a_dtype == MOE_DT_BF16 ? 0 : (rows + 1) * (size_t)(inter_dim / 32));
+  w.groups = o;   o += moe_align256((size_t)cap_tiles * 8) + 256;
+  w.cgroups = o;  o += moe_align256((size_t)cap_tiles * 8) + 256;
+  w.tile_hot = o; o += moe_align256((size_t)cap_tiles * 4);
+  w.hot_e = o;    o += 256;
+  w.hotpos = o;   o += moe_align256(t * MOE_HOT_MAX * 4);
+  w.hotw = o;     o += moe_align256(t * MOE_HOT_MAX * 4);
+  w.hotmask = o;  o += moe_align256(t * 4);
+  w.hot_out = o;  o += moe_align256(t * (size_t)model_dim * 2);
+  w.dbg = o;      o += act == MOE_ACT_NONE_TEST ? moe_align256(rows * (size_t)inter_dim * 2 * 4) : 0;
+  w.total = o;
+  return w;
+}
+
+/* Offset of the NONE_TEST debug area in the workspace. */
 static inline size_t moe_fused_debug_offset(int32_t tokens, int32_t model_dim, int32_t inter_dim,
                                             int32_t cap_tiles, int32_t block_m, int32_t a_dtype) {
-  size_t rows = (size_t)cap_tiles * block_m;
-  (void)tokens;
-  return moe_align256(rows * (size_t)model_dim * moe_rowout_elem_bytes(a_dtype)) +
-         moe_align256(rows * moe_row_bytes(inter_dim, a_dtype)) +
-         moe_align256(a_dtype == MOE_DT_BF16 ? 0 : rows * (size_t)(inter_dim / 32)) +
-         moe_align256((size_t)cap_tiles * 8) + 256;
+  return moe_fused_ws_parts(tokens, model_dim, inter_dim, cap_tiles, block_m, a_dtype, MOE_ACT_NONE_TEST).dbg;
 }
 
 static inline size_t moe_fused_ws_bytes(int32_t tokens, int32_t model_dim, int32_t inter_dim,
                                         int32_t cap_tiles, int32_t block_m, int32_t a_dtype,
                                         int32_t act) {
-  size_t b = moe_fused_debug_offset(tokens, model_dim, inter_dim, cap_tiles, block_m, a_dtype);
-  if (act == MOE_ACT_NONE_TEST) b += moe_align256((size_t)cap_tiles * block_m * inter_dim * 2 * 4);
-  return b;
+  return moe_fused_ws_parts(tokens, model_dim, inter_dim, cap_tiles, block_m, a_dtype, act).total;
 }
 
 /* moe_sort -- build the padded expert-major layout (PR 5118 "Summary"; PR 6259 Stage1 input).

@@ -127,19 +127,36 @@ def rowout_elem_bytes(a_dtype):
     return 2
 
 
-def fused_debug_offset(tokens, model_dim, inter_dim, cap, block_m, a_dtype):
+HOT_MAX = 16
+WS_PARTS = ("rowout", "inter", "iscale", "groups", "cgroups", "tile_hot", "hot_e", "hotpos", "hotw", "hotmask",
+            "hot_out", "dbg", "total")
+
+
+def fused_ws_parts(tokens, model_dim, inter_dim, cap, block_m, a_dtype, act):
+    """Byte offsets of the workspace parts and the total (moe_fused_ws_parts of the header)."""
     rows = cap * block_m
-    return (_align256(rows * model_dim * rowout_elem_bytes(a_dtype))
-            + _align256(rows * row_bytes(inter_dim, a_dtype))
-            + _align256(0 if a_dtype == DT_BF16 else rows * (inter_dim // 32))
-            + _align256(cap * 8) + 256)
+    t = max(tokens, 0)
+    sizes = [_align256(rows * model_dim * rowout_elem_bytes(a_dtype)),
+             _align256((rows + 1) * row_bytes(inter_dim, a_dtype)),
+             _align256(0 if a_dtype == DT_BF16 else (rows + 1) * (inter_dim // 32)),
+             _align256(cap * 8) + 256, _align256(cap * 8) + 256, _align256(cap * 4), 256,
+             _align256(t * HOT_MAX * 4), _align256(t * HOT_MAX * 4), _align256(t * 4),
+             _align256(t * model_dim * 2),
+             _align256(rows * inter_dim * 2 * 4) if act == ACT_NONE_TEST else 0]
+    out, o = {}, 0
+    for name, sz in zip(WS_PARTS, sizes):
+        out[name] = o
+        o += sz
+    out["total"] = o
+    return out
+
+
+def fused_debug_offset(tokens, model_dim, inter_dim, cap, block_m, a_dtype):
+    return fused_ws_parts(tokens, model_dim, inter_dim, cap, block_m, a_dtype, ACT_NONE_TEST)["dbg"]
 
 
 def fused_ws_bytes(tokens, model_dim, inter_dim, cap, block_m, a_dtype, act):
-    b = fused_debug_offset(tokens, model_dim, inter_dim, cap, block_m, a_dtype)
-    if act == ACT_NONE_TEST:
-        b += _align256(cap * block_m * inter_dim * 2 * 4)
-    return b
+    return fused_ws_parts(tokens, model_dim, inter_dim, cap, block_m, a_dtype, act)["total"]
 
 
 # ------------------------------------------------------------------ entry points

@@ -156,14 +156,10 @@ moe_status_t fused_call(const void* x, const uint8_t* x_scale, int32_t a_dtype, 
   }
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
 
-  const size_t rows = (size_t)layout->cap_tiles * layout->block_m;
   uint8_t* base = (uint8_t*)ws;
-  const size_t off_inter = moe_align256(rows * (size_t)model_dim * moe_rowout_elem_bytes(a_dtype));
-  const size_t off_iscale = off_inter + moe_align256(rows * moe_row_bytes(inter_dim, a_dtype));
-  const size_t off_groups = off_iscale + moe_align256(a_dtype == MOE_DT_BF16 ? 0 : rows * (size_t)(inter_dim / 32));
-  const size_t off_ngroups = off_groups + moe_align256((size_t)layout->cap_tiles * 8);
-  const size_t off_dbg = moe_fused_debug_offset(tokens, model_dim, inter_dim, layout->cap_tiles,
-                                                layout->block_m, a_dtype);
+  const moe_fused_ws_parts_t W = moe_fused_ws_parts(tokens, model_dim, inter_dim, layout->cap_tiles,
+                                                    layout->block_m, a_dtype, act->act);
+  const size_t groups_bytes = moe_align256((size_t)layout->cap_tiles * 8);
   moe::FusedArgs a;
   a.x = (const uint8_t*)x;
   a.xs = x_scale;
@@ -175,13 +171,21 @@ moe_status_t fused_call(const void* x, const uint8_t* x_scale, int32_t a_dtype, 
   a.sorted_ids = layout->sorted_token_ids;
   a.expert_ids = layout->expert_ids;
   a.num_tiles = layout->num_tiles;
-  a.rowout = base;
-  a.groups = (int2*)(base + off_groups);
-  a.num_groups = (int32_t*)(base + off_ngroups);
+  a.rowout = base + W.rowout;
+  a.groups = (int2*)(base + W.groups);
+  a.num_groups = (int32_t*)(base + W.groups + groups_bytes);
+  a.cgroups = (int2*)(base + W.cgroups);
+  a.num_cgroups = (int32_t*)(base + W.cgroups + groups_bytes);
+  a.tile_hot = (int32_t*)(base + W.tile_hot);
+  a.hot_e = (int32_t*)(base + W.hot_e);
+  a.hotpos = (int32_t*)(base + W.hotpos);
+  a.hotw = (float*)(base + W.hotw);
+  a.hotmask = (uint32_t*)(base + W.hotmask);
+  a.hot_out = base + W.hot_out;
   a.row_of = layout->row_of;
-  a.inter = base + off_inter;
-  a.inter_s = a_dtype == MOE_DT_BF16 ? nullptr : base + off_iscale;
-  a.dbg = act->act == MOE_ACT_NONE_TEST ? (float*)(base + off_dbg) : nullptr;
+  a.inter = base + W.inter;
+  a.inter_s = a_dtype == MOE_DT_BF16 ? nullptr : base + W.iscale;
+  a.dbg = act->act == MOE_ACT_NONE_TEST ? (float*)(base + W.dbg) : nullptr;
   a.sync = layout->sync;
   a.out = out_bf16;
   a.T = tokens;

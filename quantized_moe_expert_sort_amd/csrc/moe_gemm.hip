@@ -49,24 +49,43 @@ __global__ __launch_bounds__(THREADS, MINW) void stage2_kernel(FusedArgs p, int 
 // out[t, c] = sum over k (ascending) of rowout[row_of[t*topk + k], c], in fp32, rounded to
 // bf16.  Thread = 8 consecutive columns of one token; rows of non-local experts (-1) are skipped.
 // W: the rows were stored without the router weight (grouped Stage2); each is multiplied by
-// topk_w[t*topk + k] in fp32 before it is added.
+// topk_w[t*topk + k] in fp32 before it is added.  hot_e (with W, may be null): when it lists hot
+// experts, a token's slots in hotmask[t] were summed token-major into hot_out[t] (router weight
+// applied); the sum then starts from that row and skips those slots.
 
 template <bool W = false>
 __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restrict__ rowout,
                                                           const int32_t* __restrict__ row_of,
                                                           uint16_t* __restrict__ out, int T, int topk,
-                                                          int D, const float* __restrict__ topk_w = nullptr) {
+                                                          int D, const float* __restrict__ topk_w = nullptr,
+                                                          const int32_t* __restrict__ hot_e = nullptr,
+                                                          const uint32_t* __restrict__ hotmask = nullptr,
+                                                          const uint8_t* __restrict__ hot_out = nullptr) {
   const int groups = D / 8;
   const int64_t idx = (int64_t)blockIdx.x * THREADS + threadIdx.x;
   if (idx >= (int64_t)T * groups) return;
   const int t = (int)(idx / groups), c = (int)(idx - (int64_t)t * groups) * 8;
   float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  uint32_t hmask = 0;
+  if (W && hot_e && hot_e[MOE_HOT_MAX] > 0) {
+    hmask = hotmask[t];
+    if (hmask) {
+      const uint4 q = *reinterpret_cast<const uint4*>(hot_out + ((size_t)t * D + c) * 2);
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        sum[2 * h] = __uint_as_float(w4[h] << 16);
+        sum[2 * h + 1] = __uint_as_float(w4[h] & 0xFFFF0000u);
+      }
+    }
+  }
   // all row indices of a group of KG slots first, then all their row loads, then the sums
   constexpr int KG = 8;
   for (int k0 = 0; k0 < topk; k0 += KG) {
     int r[KG];
 #pragma unroll
-    for (int u = 0; u < KG; ++u) r[u] = k0 + u < topk ? row_of[(int64_t)t * topk + k0 + u] : -1;
+    for (int u = 0; u < KG; ++u)
+      r[u] = k0 + u < topk && !((hmask >> (k0 + u)) & 1u) ? row_of[(int64_t)t * topk + k0 + u] : -1;
     uint4 q[KG];
     float wk[KG];
 #pragma unroll
@@ -310,7 +329,8 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
   const int64_t nthreads = (int64_t)a.T * (a.D / 8);
   const unsigned gridc = (unsigned)((nthreads + THREADS - 1) / THREADS);
   if (tiled2)   // grouped Stage2 rows carry no router weight
-    combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, a.topk_w);
+    combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, a.topk_w,
+                                                   hot_path(a) ? a.hot_e : nullptr, a.hotmask, a.hot_out);
   else
     combine_kernel<false><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
   return hipGetLastError();

@@ -66,6 +66,7 @@ static_assert(WM * WN == GWAVES, "wave grid");
 
 constexpr int GROUP_THREADS = 1024;
 constexpr int GROUP_LDS_TILES = 16384;
+constexpr int HOT_MAX_G = MOE_HOT_MAX;
 
 __device__ __forceinline__ int group_size(int len) {
   const int ng = (len + GT - 1) / GT;
@@ -73,12 +74,21 @@ __device__ __forceinline__ int group_size(int len) {
 }
 
 static_assert(GROUP_LDS_TILES % GROUP_THREADS == 0, "whole loads per thread");
+// Besides the groups, the same passes pick the hot experts of the token-major Stage2 (below): an
+// expert whose run has at least hot_min_tiles tiles is hot, hot indices follow the expert order
+// up to MOE_HOT_MAX; every tile gets its expert's hot index (or -1) in tile_hot, the hot experts
+// go to hot_e (their count at hot_e[MOE_HOT_MAX]) and the groups of the other experts, in order,
+// to cgroups.
 __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __restrict__ expert_ids,
                                                               const int32_t* __restrict__ num_tiles_p,
                                                               int cap, int2* __restrict__ groups,
-                                                              int32_t* __restrict__ num_groups) {
+                                                              int32_t* __restrict__ num_groups, int hot_min_tiles,
+                                                              int2* __restrict__ cgroups,
+                                                              int32_t* __restrict__ num_cgroups,
+                                                              int32_t* __restrict__ tile_hot,
+                                                              int32_t* __restrict__ hot_e) {
   __shared__ int lds_e[GROUP_LDS_TILES];
-  __shared__ int tmp[GROUP_THREADS / WAVE + 1];
+  __shared__ int tmp[3][GROUP_THREADS / WAVE + 1];
   const int n = min(*num_tiles_p, cap);
   const bool in_lds = n <= GROUP_LDS_TILES;
   if (in_lds) {   // GROUP_LDS_TILES / GROUP_THREADS loads per thread, all issued before the stores
@@ -100,7 +110,7 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __r
   // memory (a select between the two would become a generic-address load on every step)
   auto work = [&](auto E) {
     const int per = (n + GROUP_THREADS - 1) / GROUP_THREADS;
-    const int t0 = threadIdx.x * per, t1 = min(n, t0 + per);
+    const int t0 = min(n, (int)threadIdx.x * per), t1 = min(n, t0 + per);
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 
     // run bounds [rs, re) of tile t's expert e = E(t), found by galloping outwards from t (steps
@@ -129,38 +139,92 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __r
       cur_e = e;
       re = run_end(t, e);
     };
-    int starts = 0;
+    // pass 1: groups, hot runs starting here, groups of the runs that are not hot
+    int starts = 0, hot_here = 0;
     for (int t = t0; t < t1; ++t) {
       bounds(t);
       starts += ((t - rs) % group_size(re - rs)) == 0;
+      hot_here += t == rs && re - rs >= hot_min_tiles;
     }
-    int scan = starts;
+    // exclusive scans of the three counts over the workgroup (cold groups: after hot indices)
+    auto scan3 = [&](int v0, int v1, int (&ex)[2], int (&tot)[2]) {
+      int vv[2] = {v0, v1};
 #pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-      const int o = __shfl_up(scan, d, WAVE);
-      if (lane >= d) scan += o;
+      for (int q = 0; q < 2; ++q) {
+        int sc = vv[q];
+#pragma unroll
+        for (int d = 1; d < WAVE; d <<= 1) {
+          const int o = __shfl_up(sc, d, WAVE);
+          if (lane >= d) sc += o;
+        }
+        if (lane == WAVE - 1) tmp[q][w] = sc;
+        vv[q] = sc;
+      }
+      __syncthreads();
+      if (threadIdx.x < 2) {
+        int run = 0;
+        for (int i = 0; i < GROUP_THREADS / WAVE; ++i) { const int c = tmp[threadIdx.x][i]; tmp[threadIdx.x][i] = run; run += c; }
+        tmp[threadIdx.x][GROUP_THREADS / WAVE] = run;
+      }
+      __syncthreads();
+      ex[0] = tmp[0][w] + vv[0] - v0;
+      ex[1] = tmp[1][w] + vv[1] - v1;
+      tot[0] = tmp[0][GROUP_THREADS / WAVE];
+      tot[1] = tmp[1][GROUP_THREADS / WAVE];
+      __syncthreads();
+    };
+    int ex[2], tot[2];
+    scan3(starts, hot_here, ex, tot);
+    const int hbase = ex[1];
+    const int nh = min(tot[1], HOT_MAX_G);
+    // the hot index of tile t's run: runs starting in this chunk count from hbase, a run that
+    // started before the chunk is the last hot run before it
+    auto hot_index = [&](int t, int h_next) {
+      if (re - rs < hot_min_tiles) return -1;
+      const int h = rs >= t0 ? h_next : hbase - 1;
+      return h < HOT_MAX_G ? h : -1;
+    };
+    int cold_here = 0;
+    cur_e = INT32_MIN;
+    {
+      int hn = hbase;
+      for (int t = t0; t < t1; ++t) {
+        bounds(t);
+        const int h = hot_index(t, t == rs ? hn : hn - 1);
+        if (t == rs && re - rs >= hot_min_tiles) ++hn;
+        cold_here += h < 0 && ((t - rs) % group_size(re - rs)) == 0;
+      }
     }
-    if (lane == WAVE - 1) tmp[w] = scan;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int run = 0;
-      for (int i = 0; i < GROUP_THREADS / WAVE; ++i) { const int c = tmp[i]; tmp[i] = run; run += c; }
-      tmp[GROUP_THREADS / WAVE] = run;
-    }
-    __syncthreads();
-    int gidx = tmp[w] + scan - starts;
+    int ex2[2], tot2[2];
+    scan3(cold_here, 0, ex2, tot2);
+    int gidx = ex[0], cidx = ex2[0], hn = hbase;
     cur_e = INT32_MIN;
     for (int t = t0; t < t1; ++t) {
       bounds(t);
+      const bool start_run = t == rs && re - rs >= hot_min_tiles;
+      const int h = hot_index(t, t == rs ? hn : hn - 1);
+      if (start_run) {
+        if (hn < HOT_MAX_G) hot_e[hn] = cur_e;
+        ++hn;
+      }
+      tile_hot[t] = h;
       const int gs = group_size(re - rs);
-      if ((t - rs) % gs == 0) groups[gidx++] = int2{t, min(gs, re - t)};
+      if ((t - rs) % gs == 0) {
+        const int2 gr = int2{t, min(gs, re - t)};
+        groups[gidx++] = gr;
+        if (h < 0) cgroups[cidx++] = gr;
+      }
+    }
+    if (threadIdx.x == 0) {
+      *num_groups = tot[0];
+      *num_cgroups = tot2[0];
+      hot_e[HOT_MAX_G] = nh;
     }
   };
   if (in_lds)
     work([&](int i) { return lds_e[i]; });
   else
     work([&](int i) { return expert_ids[i]; });
-  if (threadIdx.x == 0) *num_groups = tmp[GROUP_THREADS / WAVE];
 }
 
 // ---------------------------------------------------------------- load-to-LDS copies
@@ -899,6 +963,277 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
   }
 }
 
+// ---------------------------------------------------------------- token-major Stage2 of hot experts
+//
+// With a skewed routing a few experts are chosen by a large share of the tokens (the prefill
+// workload's Zipf prior: the top 16 experts hold ~64% of the routed rows).  Their Stage2 rows are
+// taken token-major: an item is 128 consecutive tokens x 256 output columns and loops over the hot
+// experts, gathering for each the intermediate rows of the item's tokens (the workspace's zero row
+// for a token that does not route to it), so the router-weighted contributions of all hot experts
+// to a token add up in registers and one bf16 partial row per token is stored, instead of one row
+// per (token, hot expert) that the combine would read back.  The other experts' groups take the
+// grouped Stage2 as before, and the combine adds the token's partial row to its other rows.
+// An expert is hot when its rows are at least a quarter of the tokens (so at most a quarter of an
+// item's MFMA rows are zero rows), up to MOE_HOT_MAX experts in ascending expert order.
+
+constexpr int HOT_MAX = MOE_HOT_MAX;
+// Thread = token: its layout row and router weight for each hot expert (the zero row and 0 for a
+// hot expert it does not route to) and the mask of its slots whose expert is hot; workgroup 0
+// also clears the zero row of the intermediate.  Nothing is written when no expert is hot.
+constexpr int TABLE_THREADS = 256;
+__global__ __launch_bounds__(TABLE_THREADS) void hot_table_kernel(FusedArgs p, int zrow, int row_bytes) {
+  const int nh = p.hot_e[HOT_MAX];
+  if (nh == 0) return;
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < row_bytes; i += TABLE_THREADS) p.inter[(size_t)zrow * row_bytes + i] = 0;
+    if (p.inter_s)
+      for (int i = threadIdx.x; i < p.I / 32; i += TABLE_THREADS) p.inter_s[(size_t)zrow * (p.I / 32) + i] = 0;
+  }
+  const int t = blockIdx.x * TABLE_THREADS + threadIdx.x;
+  if (t >= p.T) return;
+  int32_t* pos = p.hotpos + (size_t)t * HOT_MAX;
+  float* wt = p.hotw + (size_t)t * HOT_MAX;
+#pragma unroll
+  for (int h = 0; h < HOT_MAX; ++h) {
+    pos[h] = zrow;
+    wt[h] = 0.f;
+  }
+  uint32_t mask = 0;
+  for (int k = 0; k < p.topk; ++k) {
+    const int64_t v = (int64_t)t * p.topk + k;
+    const int r = p.row_of[v];
+    if (r < 0) continue;
+    const int h = p.tile_hot[r / 32];
+    if (h < 0) continue;
+    pos[h] = r;
+    wt[h] = p.topk_w[v];
+    mask |= 1u << k;
+  }
+  p.hotmask[t] = mask;
+}
+
+// LDS operand staging of the token-major items: P buffers [A tile 128 rows | B tile 256 weight
+// rows | A scale dwords | B scale dwords], then the item's tables of layout rows and router
+// weights (128 tokens x MOE_HOT_MAX each) and the hot experts.
+template <int ADT>
+struct HFmt {
+  static constexpr int BM = 128;                          // tokens per item
+  static constexpr int MF = BM / WM / 16;                 // 16-row fragments per wave: 4
+  static constexpr int KA = ADT == DT_FP8 ? 128 : 64;     // A bytes per row per K step
+  static constexpr int ACPR = KA / 16;
+  static constexpr int P = ADT == DT_FP4 ? 5 : 4;         // LDS buffers
+  static constexpr int A_BYTES = BM * KA;
+  static constexpr int B_BYTES = BNW * 64;
+  static constexpr int BUF = A_BYTES + B_BYTES + (BM + BNW) * 4;
+  static constexpr int A_IPL = A_BYTES / 1024 / NLOAD;    // A copy instructions per loader per step
+  static constexpr int B_IPL = B_BYTES / 1024 / NLOAD;
+  static constexpr int TAB = BM * HOT_MAX;                // entries per table
+  static constexpr int BYTES = P * BUF + 2 * TAB * 4;
+};
+
+template <int ADT>
+__global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, int zrow) {
+  using F = HFmt<ADT>;
+  constexpr int KA = F::KA, ACPR = F::ACPR, P = F::P, BM = F::BM, MF = F::MF;
+  static_assert(F::A_IPL * NLOAD * 1024 == F::A_BYTES && F::B_IPL * NLOAD * 1024 == F::B_BYTES, "copy split");
+  static_assert(F::BYTES <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[F::BYTES];
+  __shared__ int s_hot[HOT_MAX];
+  int32_t* tpos = reinterpret_cast<int32_t*>(lds + P * F::BUF);
+  float* tw = reinterpret_cast<float*>(lds + P * F::BUF + F::TAB * 4);
+
+  const int nh = ld_const(p.hot_e + HOT_MAX);
+  if (nh == 0) return;
+  const int D = p.D, I = p.I, T = p.T;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
+  const bool loader = wave < NLOAD;
+  const int lw = wave & (NLOAD - 1);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+  const int S = I / 128, SS = nh * S;                     // K steps per expert, per item
+  const uint32_t lds0 = lds_addr(lds);
+  const uint32_t a_rowbytes = (uint32_t)(I * KA / 128);
+  if (threadIdx.x < HOT_MAX) s_hot[threadIdx.x] = p.hot_e[threadIdx.x];
+
+  // items in column-block-major order, cut into 8 contiguous ranges, one per XCD: an XCD touches
+  // the weight rows of at most a few column blocks (they stay in its L2) while every token tile's
+  // gathered rows come from the memory-side cache
+  const int ntl = (T + BM - 1) / BM, n_nblk = D / BNW, n_items = ntl * n_nblk;
+  const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
+  const int it_lo = (int)((int64_t)n_items * xcd / 8), it_hi = (int)((int64_t)n_items * (xcd + 1) / 8);
+
+  // the item's tables: layout row of (token, hot expert) and its router weight; tokens past T
+  // read the zero row with weight 0 (loaded by the loader waves, whose only stores still in flight
+  // are those of the item before)
+  auto load_tables = [&](int item) {
+    const int tl = item % ntl;
+    const int tok0 = tl * BM;
+    constexpr int PER = F::TAB / (NLOAD * WAVE);          // entries per loader lane: 8
+    int vp[PER];
+    float vw[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = (u * NLOAD + lw) * WAVE + lane;
+      const int tok = tok0 + i / HOT_MAX;
+      vp[u] = tok < T ? p.hotpos[(size_t)tok * HOT_MAX + (i % HOT_MAX)] : zrow;
+      vw[u] = tok < T ? p.hotw[(size_t)tok * HOT_MAX + (i % HOT_MAX)] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = (u * NLOAD + lw) * WAVE + lane;
+      tpos[i] = vp[u];
+      tw[i] = vw[u];
+    }
+  };
+  // copies of step ss (expert ss / S, K step ss % S) of item `item` into buffer buf
+  auto issue = [&](int item, int ss, int buf) {
+    const int hh = ss / S, s = ss - hh * S;
+    const int nb = item / ntl;
+    const int e = s_hot[hh];
+    const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * F::BUF);
+    const uint8_t* ab = p.inter + s * KA;
+    const uint8_t* bb = p.w2 + (size_t)e * D * (I / 2) + s * 64;
+#pragma unroll
+    for (int i = 0; i < F::A_IPL; ++i) {
+      const int j = i * NLOAD + lw;
+      const int q = j * WAVE + lane;
+      const int row = q / ACPR, part = swz_slot<ACPR>(row, q % ACPR) - row * ACPR;
+      const int r = tpos[row * HOT_MAX + hh];
+      dma16(ab, (uint32_t)r * a_rowbytes + part * 16, L + j * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < F::B_IPL; ++i) {
+      const int j = i * NLOAD + lw;
+      const int q = j * WAVE + lane;
+      const int row = q / 4, part = swz_slot<4>(row, q % 4) - row * 4;
+      dma16(bb, (uint32_t)(nb * BNW + row) * (uint32_t)(I / 2) + part * 16, L + F::A_BYTES + j * 1024);
+    }
+    const int sc = lw * WAVE + lane;
+    if (lw * WAVE < BM) {
+      const int r = tpos[min(sc, BM - 1) * HOT_MAX + hh];
+      dma4(p.inter_s + s * 4, (uint32_t)r * (uint32_t)(I / 32), L + F::A_BYTES + F::B_BYTES + lw * 256);
+    }
+    dma4(p.w2s + (size_t)e * D * (I / 32) + s * 4, (uint32_t)(nb * BNW + sc) * (uint32_t)(I / 32),
+         L + F::A_BYTES + F::B_BYTES + BM * 4 + lw * 256);
+  };
+  // copy instructions a loader issues per step
+  const int per_step = F::A_IPL + F::B_IPL + 1 + (lw * WAVE < BM ? 1 : 0);
+
+  const int arow0 = (BM / WM) * wm;
+  int item = it_lo + local0;
+  if (item < it_hi && loader) {
+    load_tables(item);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  lds_barrier();                                          // tables and hot experts are in LDS
+  if (item < it_hi && loader) {
+#pragma unroll
+    for (int q = 0; q < P - 1; ++q)
+      if (q < SS) issue(item, q, q);
+  }
+  int n_st = 0;
+  for (; item < it_hi; item += stride) {
+    const int nxt = item + stride;
+    v4f acc[MF][NFW], tmp[MF][NFW];
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+#pragma unroll
+      for (int j = 0; j < NFW; ++j) acc[f][j] = tmp[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf) {
+      const uint8_t* la = lds + buf * F::BUF;
+      const uint8_t* lb = la + F::A_BYTES;
+      const uint32_t* las = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
+      const uint32_t* lbs = las + BM;
+      v8i wop[NFW];
+      uint32_t wsc[NFW];
+#pragma unroll
+      for (int j = 0; j < NFW; ++j) {
+        const int br = 64 * wn + (j >> 1) * 32 + 8 * (r16 >> 2) + 4 * (j & 1) + (r16 & 3);
+        wop[j] = fp4_operand_lo(*reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16));
+        wsc[j] = (lbs[br] >> (8 * g)) & 0xFFu;
+      }
+      auto load_x = [&](int f, v8i& xop, uint32_t& xsc) {
+        const int ar = arow0 + 16 * f + r16;
+        if (ADT == DT_FP8) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, g) * 16);
+          const uint4 hi = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, 4 + g) * 16);
+          xop = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else {
+          xop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
+        }
+        xsc = (las[ar] >> (8 * g)) & 0xFFu;
+      };
+      v8i x_cur;
+      uint32_t xs_cur;
+      load_x(0, x_cur, xs_cur);
+#pragma unroll
+      for (int f = 0; f < MF; ++f) {
+        v8i x_nxt = x_cur;
+        uint32_t xs_nxt = xs_cur;
+        if (f + 1 < MF) load_x(f + 1, x_nxt, xs_nxt);
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) tmp[f][j] = mfma_w_x<ADT>(wop[j], x_cur, tmp[f][j], wsc[j], xs_cur);
+        __builtin_amdgcn_sched_barrier(0);
+        x_cur = x_nxt;
+        xs_cur = xs_nxt;
+      }
+    };
+
+    for (int ss = 0; ss < SS; ++ss) {
+      wait_and_barrier(loader ? per_step * min(SS - 1 - ss, P - 2) + (ss < P - 1 ? n_st : 0) : 63);
+      if (loader && ss + P - 1 < SS) issue(item, ss + P - 1, (ss + P - 1) % P);
+      compute(ss % P);
+      if ((ss + 1) % S == 0) {                             // the expert's last K step: weight and add
+        const int hh = ss / S;
+#pragma unroll
+        for (int f = 0; f < MF; ++f) {
+          const float wv = tw[(arow0 + 16 * f + r16) * HOT_MAX + hh];
+#pragma unroll
+          for (int j = 0; j < NFW; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[f][j][i] += wv * tmp[f][j][i];
+            tmp[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      }
+    }
+    lds_barrier();                                        // every operand and table read is done
+    const int tok_base = (item % ntl) * BM;
+    const int nb = item / ntl;
+    if (nxt < it_hi && loader) {
+      load_tables(nxt);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_barrier();                                        // the next item's tables are in LDS
+    if (nxt < it_hi && loader) {
+#pragma unroll
+      for (int q = 0; q < P - 1; ++q)
+        if (q < SS) issue(nxt, q, q);
+    }
+    // token arow0 + 16 f + r16, output columns 64 wn + 8 g .. + 7 and 64 wn + 32 + 8 g .. + 7.
+    // The loaders' first waits of the next item let these stores stay in flight: counted only
+    // when every one of them is issued (a tile wholly below T), else none (the wait is stricter)
+    const bool full_tile = tok_base + BM <= T;
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+      const int tok = tok_base + arow0 + 16 * f + r16;
+      uint32_t d[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        d[k] = (uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1)]) |
+               ((uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1) + 1]) << 16);
+      if (tok < T) {
+        uint8_t* o = p.hot_out + ((size_t)tok * D + (size_t)nb * BNW + 64 * wn + 8 * g) * 2;
+        *reinterpret_cast<uint4*>(o) = uint4{d[0], d[1], d[2], d[3]};
+        *reinterpret_cast<uint4*>(o + 64) = uint4{d[4], d[5], d[6], d[7]};
+      }
+    }
+    n_st = full_tile ? 2 * MF : 0;
+  }
+}
+
 // Compute units of the current device, queried at each launch (a host call of about a
 // microsecond next to kernels of hundreds): no state shared between threads or devices.
 int num_cus() {
@@ -913,6 +1248,17 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
   const int n_nblk = STAGE == 1 ? (2 * a.I) / BNW : a.D / BNW;
   const unsigned grid = (unsigned)(num_cus() / 8 * 8);    // one workgroup per CU, a multiple of 8
   if constexpr (STAGE == 2) {
+    if constexpr (ADT != DT_BF16) {
+      if (hot_path(a)) {   // hot experts token-major, the other experts' groups below
+        const int zrow = a.cap_tiles * a.block_m;
+        const int row_bytes = ADT == DT_FP8 ? a.I : a.I / 2;
+        hot_table_kernel<<<(unsigned)((a.T + TABLE_THREADS - 1) / TABLE_THREADS), TABLE_THREADS, 0, s>>>(a, zrow,
+                                                                                                      row_bytes);
+        hot_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, zrow);
+        groups = a.cgroups;
+        ngroups = a.num_cgroups;
+      }
+    }
     grouped_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   } else if (a.act == ACT_SITUV2)
     grouped_stage1_kernel<ADT, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
@@ -922,6 +1268,11 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
 }
 
 }  // namespace
+
+bool hot_path(const FusedArgs& a) {
+  // fp8 / fp4 intermediates, slots fit the 32-bit mask, the large-batch Stage2
+  return a.a_dtype != DT_BF16 && a.topk <= 32 && tiled_path_supported(a) && a.T >= TILED_MIN_TOKENS_S2;
+}
 
 bool tiled_path_supported(const FusedArgs& a) {
   // the A copies address the activation rows with 32-bit offsets
@@ -933,7 +1284,10 @@ bool tiled_path_supported(const FusedArgs& a) {
 hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipStream_t s) {
   hipError_t err;
   if (a.stages & 1) {
-    group_kernel<<<1, GROUP_THREADS, 0, s>>>(a.expert_ids, a.num_tiles, a.cap_tiles, groups, ngroups);
+    // hot experts: rows at least a quarter of the tokens (tiles of 32 rows)
+    const int hot_min_tiles = hot_path(a) ? (a.T + 4 * 32 - 1) / (4 * 32) : INT32_MAX;
+    group_kernel<<<1, GROUP_THREADS, 0, s>>>(a.expert_ids, a.num_tiles, a.cap_tiles, groups, ngroups, hot_min_tiles,
+                                             a.cgroups, a.num_cgroups, a.tile_hot, a.hot_e);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     err = a.a_dtype == DT_FP8   ? launch_grouped_stage<DT_FP8, 1>(a, groups, ngroups, s)
           : a.a_dtype == DT_FP4 ? launch_grouped_stage<DT_FP4, 1>(a, groups, ngroups, s)

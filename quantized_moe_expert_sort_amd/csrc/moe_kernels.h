@@ -44,6 +44,14 @@ struct FusedArgs {
   uint8_t* inter_s;        // [cap*bm, I/32] intermediate scales (fp8 / fp4)
   int2* groups;            // [cap] tile groups (large-batch path)
   int32_t* num_groups;     // [1]
+  int2* cgroups;           // [cap] the groups of experts not taken token-major by Stage2
+  int32_t* num_cgroups;    // [1]
+  int32_t* tile_hot;       // [cap] hot index of each tile's expert, or -1
+  int32_t* hot_e;          // [MOE_HOT_MAX] hot experts, then their count at [MOE_HOT_MAX]
+  int32_t* hotpos;         // [T, MOE_HOT_MAX] layout row of (token, hot expert) or the zero row
+  float* hotw;             // [T, MOE_HOT_MAX] router weight of (token, hot expert) or 0
+  uint32_t* hotmask;       // [T] slots whose expert is hot
+  uint8_t* hot_out;        // [T, D] bf16 router-weighted sum of the token's hot-expert rows
   float* dbg;              // [cap*bm, 2I] raw gate/up sums (NONE_TEST) or null
   int32_t* sync;           // completion counters of the single-launch path or null
   uint16_t* out;           // [T, D] bf16
@@ -57,6 +65,8 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
 // Large-batch stages (moe_gemm_grouped.hip): tile groups of one expert, LDS-tiled GEMMs.
 // The tile groups are built with Stage1, so Stage2 takes the grouped path only where Stage1 does.
 bool tiled_path_supported(const FusedArgs& a);
+// Whether the large-batch Stage2 takes the hot experts token-major (then the combine adds hot_out).
+bool hot_path(const FusedArgs& a);
 hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipStream_t s);
 constexpr int TILED_MIN_TOKENS_S1 = 2048;   // Stage1 from this batch size
 constexpr int TILED_MIN_TOKENS_S2 = 2048;   // Stage2 from this batch size

@@ -133,15 +133,13 @@ class RequantExplainer:
     evaluated on the GPU's own intermediate.  Everything is decoded with the oracle's codecs."""
 
     def __init__(self, got, ws_host, row_of, inter, tokens, a_dtype, act, beta, linear_beta, w2, w2s, topk_ids,
-                 topk_w, expert_begin, model_dim, inter_dim, layout_rows, tol, rel_eps=1e-5):
+                 topk_w, expert_begin, model_dim, inter_dim, layout_rows, tol, off_c, off_s, rel_eps=1e-5):
+        """off_c, off_s: byte offsets of the intermediate codes and scales in the workspace."""
         from oracle import mx_formats as mx
         self.mx = mx
         self.fmt = {"fp8": "e4m3", "fp4": "e2m1"}[a_dtype]
         I, D = inter_dim, model_dim
         rb = I if a_dtype == "fp8" else I // 2
-        align = lambda b: (b + 255) & ~255
-        off_c = align(layout_rows * D * 2)
-        off_s = off_c + align(layout_rows * rb)
         ws_host = np.asarray(ws_host, dtype=np.uint8)
         self.codes = ws_host[off_c:off_c + layout_rows * rb].reshape(layout_rows, rb)
         self.scales = ws_host[off_s:off_s + layout_rows * (I // 32)].reshape(layout_rows, I // 32)

@@ -44,6 +44,30 @@ def test_block_m_rule_matches_header_and_inputs():
         assert gen.Workload("w", t, 8, 2, 256, 128, "bf16").block_m == want
 
 
+def test_workspace_layout_matches_header(tmp_path):
+    # the binding mirrors the header's static inline layout helpers: compile the header with gcc
+    # and compare every offset for a spread of shapes
+    cases = [(1, 3584, 384, 17, 16, 0, 0), (4, 256, 128, 9, 16, 1, 2), (16384, 3584, 384, 9088, 32, 2, 0),
+             (8192, 3584, 3072, 4208, 32, 1, 1), (0, 512, 256, 0, 16, 0, 0), (3000, 1024, 384, 950, 32, 2, 2)]
+    prog = ['#include <stdio.h>', '#include "moe_mi355x.h"', "int main(void) {"]
+    for c in cases:
+        prog.append("  { moe_fused_ws_parts_t w = moe_fused_ws_parts(%d, %d, %d, %d, %d, %d, %d);" % c)
+        prog.append('    printf("' + " ".join(["%zu"] * len(qm.WS_PARTS)) + '\\n", ' +
+                    ", ".join("w." + n for n in qm.WS_PARTS) + "); }")
+    prog.append("  return 0; }")
+    src = tmp_path / "ws.c"
+    src.write_text("\n".join(prog))
+    exe = tmp_path / "ws"
+    import subprocess
+    subprocess.run(["gcc", "-O1", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    for c, line in zip(cases, lines):
+        got = [int(v) for v in line.split()]
+        want = qm.fused_ws_parts(*c)
+        assert got == [want[n] for n in qm.WS_PARTS], c
+        assert qm.fused_ws_bytes(*c) == want["total"]
+
+
 def test_header_size_helpers_match_binding():
     # the binding mirrors the header's static inline size helpers; spot-check the formulas
     assert qm.cap_tiles(1, 16, 896, 16) == 17

@@ -59,8 +59,11 @@ def explainer(got, ws, lay, inter, tokens, a_dtype, act, host_w, ids, w, eb, D, 
     """Near-tie requantization explainer of fp8 / fp4 rows (None for bf16)."""
     if a_dtype == "bf16":
         return None
+    T = np.asarray(ids).shape[0]
+    parts = qm.fused_ws_parts(T, D, I, lay.cap, lay.block_m, qm.DTYPES[a_dtype], qm.ACTS[act])
     return RequantExplainer(got, ws.cpu().numpy(), lay.row_of.cpu().numpy(), inter, tokens, a_dtype, act, BETA, LBETA,
-                            host_w[2], host_w[3], ids, w, eb, D, I, lay.cap * lay.block_m, TOL[a_dtype])
+                            host_w[2], host_w[3], ids, w, eb, D, I, lay.cap * lay.block_m, TOL[a_dtype],
+                            parts["inter"], parts["iscale"])
 
 
 SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
@@ -93,6 +96,10 @@ SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
     (2500, 40, 6, 1024, 128, 0, 40, 32, "bf16", "silu", 0.0),
     (3000, 64, 8, 1024, 384, 16, 24, 32, "bf16", "situv2", 0.0),
     (2048, 64, 5, 512, 256, 0, 64, 32, "bf16", "situv2", 0.0),    # ~5-tile groups: parts of 3 + 2 tiles
+    # experts with at least a quarter of the tokens' rows: token-major Stage2 for up to 16 of them
+    (2048, 24, 16, 512, 256, 0, 24, 32, "fp4", "silu", 0.3),      # all 24 qualify: 16 token-major
+    (2100, 24, 16, 512, 256, 0, 24, 32, "fp8", "situv2", 0.0),    # partial last 128-token tile
+    (2600, 32, 16, 512, 256, 4, 16, 32, "fp4", "situv2", 0.0),    # expert-parallel shard, all local hot
     # the same batch sizes with model_dim % 512 != 0 take the per-tile stages
     (2500, 40, 6, 256, 128, 0, 40, 32, "fp4", "silu", 0.0),
     (3000, 64, 8, 768, 384, 16, 24, 32, "fp8", "situv2", 0.0),

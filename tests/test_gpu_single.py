@@ -87,8 +87,10 @@ def test_single_launch_matches_per_stage_bits(T, Er, K, D, I, eb, E, bm, a_dtype
                          dtype=torch.uint8, device="cuda")
         qm.moe_fused(pb["xa"], pb["xs"], a_dtype, *pb["wd"], pb["w_d"], lay_m, E, act, BETA, LBETA, ws=ws)
         torch.cuda.synchronize()
+        parts = qm.fused_ws_parts(T, D, I, lay_m.cap, bm, qm.DTYPES[a_dtype], qm.ACTS[act])
         ex = RequantExplainer(got, ws.cpu().numpy(), lay_m.row_of.cpu().numpy(), inter, None, a_dtype, act, BETA,
-                              LBETA, pb["host_w"][2], pb["host_w"][3], ids, pb["w"], eb, D, I, lay_m.cap * bm, tol)
+                              LBETA, pb["host_w"][2], pb["host_w"][3], ids, pb["w"], eb, D, I, lay_m.cap * bm, tol,
+                              parts["inter"], parts["iscale"])
     assert_rows_close(got, ref, local, tol, f"{a_dtype} {act}", explain=ex)
 
 

@@ -68,13 +68,13 @@ def _fake_workspace(a_dtype, inter, lay, D, I):
     """A moe_fused workspace holding the oracle's own intermediate codes at each row's layout
     position (what a GPU that decided exactly as the oracle would have written)."""
     from oracle import mx_formats as mx
+    import quantized_moe_expert_sort_amd as qm
     fmt = {"fp8": "e4m3", "fp4": "e2m1"}[a_dtype]
     rows = lay["cap"] * 16
     rb = I if a_dtype == "fp8" else I // 2
-    al = lambda b: (b + 255) & ~255
-    off_c = al(rows * D * 2)
-    off_s = off_c + al(rows * rb)
-    ws = np.zeros(off_s + al(rows * I // 32), np.uint8)
+    parts = qm.fused_ws_parts(len(lay["row_of"]) // 2, D, I, lay["cap"], 16, qm.DTYPES[a_dtype], qm.ACT_SITUV2)
+    off_c, off_s = parts["inter"], parts["iscale"]
+    ws = np.zeros(parts["total"], np.uint8)
     for e, (vs, g, u, _) in inter.items():
         for r, v in enumerate(vs):
             y32 = np.asarray(om.activation(g[r], u[r], "situv2", BETA, LBETA), np.float32).astype(np.float64)
@@ -82,7 +82,7 @@ def _fake_workspace(a_dtype, inter, lay, D, I):
             R = lay["row_of"][v]
             ws[off_c + R * rb:off_c + (R + 1) * rb] = mx.pack_fp4(c) if fmt == "e2m1" else c.astype(np.uint8)
             ws[off_s + R * (I // 32):off_s + (R + 1) * (I // 32)] = sc
-    return ws, off_c, rb
+    return ws, off_c, off_s, rb
 
 
 @pytest.mark.parametrize("a_dtype", ["fp8", "fp4"])
@@ -95,9 +95,10 @@ def test_requant_explainer_accepts_near_ties_only(a_dtype):
     host = gen.make_weights(4, E, D, I)
     ref, inter = om.moe_fused(x, a_dtype, *host, ids, w, 0, E, "situv2", BETA, LBETA, return_intermediate=True)
     lay = om.sort_layout(ids, 0, E, 16)
-    ws, off_c, rb = _fake_workspace(a_dtype, inter, lay, D, I)
+    ws, off_c, off_s, rb = _fake_workspace(a_dtype, inter, lay, D, I)
     mk = lambda got, ws_, eps: RequantExplainer(got, ws_, lay["row_of"], inter, None, a_dtype, "situv2", BETA, LBETA,
-                                                host[2], host[3], ids, w, 0, D, I, lay["cap"] * 16, 2e-2, rel_eps=eps)
+                                                host[2], host[3], ids, w, 0, D, I, lay["cap"] * 16, 2e-2, off_c, off_s,
+                                                rel_eps=eps)
     assert all(mk(ref, ws, 1e-5)(t) for t in range(T))          # the oracle's own codes: nothing to explain
     # change one element code of token 0's first slot where the value is far from a grid midpoint
     e, (vs, g, u, _) = next((e, it) for e, it in inter.items() if 0 in it[0].tolist())
