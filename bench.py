@@ -338,8 +338,9 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 COPY_PROBE_BYTES = 1 << 30      # elementwise float32 negation of 1 GiB: reads and writes 1 GiB
 # (workload, stage call) pairs launched by --counter-probe: the headline's dominant kernel and
 # those of the largest tiers
-PROBES = [("dec-1", 1), ("dec-1", 2), ("mid-1024", 1), ("ep-8192", 1), ("ep-8192", 2), ("pre-16384", 1),
-          ("pre-16384", 2), ("pre-a16-8192", 1), ("pre-a16-8192", 2)]
+PROBES = [("dec-1", 1), ("dec-1", 2), ("dec-4", 1), ("dec-4", 2), ("mid-1024", 1), ("mid-1024", 2),
+          ("pre-16384", 1), ("pre-16384", 2), ("pre-a16-8192", 1), ("pre-a16-8192", 2), ("ep-8192", 1),
+          ("ep-8192", 2)]
 KERNEL_KEYS = ("grouped_stage1_kernel", "grouped_stage2_kernel", "stage2_small_kernel", "stage2_kernel",
                "stage1_kernel", "combine_kernel", "group_kernel")
 
@@ -438,7 +439,7 @@ def counter_summarize(fetch_dir, write_dir, mfma_dir):
                 continue
             if bi >= 0 and bi < len(blocks):
                 tagged.append((blocks[bi], k, cs))
-            elif "neg" in k.lower() or "elementwise" in k.lower():
+            elif "neg" in k.lower():
                 tagged.append((("copy", 0), k, cs))
         return tagged
 
@@ -519,15 +520,18 @@ def cpu_info():
 
 def cpu_oracle_call_us(wl, weights_host, problem, max_experts, budget_s):
     """The oracle (routing sort + fused operator, float64) on one routing, estimated from a
-    bounded sample: the sort in full; the activation encoding on up to 512 token rows, scaled
-    to all tokens; the fused operator on up to max_experts touched experts spread over the
-    touched set, each on the tokens routed to it (the expert-major oracle's work for that
-    expert), scaled by touched / sampled.  Returns (µs per call, sampled experts, touched)."""
+    bounded sample.  The expert-major oracle's work per touched expert is the dequantization of
+    its weights (the same for every expert) plus work proportional to its routed rows; both are
+    timed on up to max_experts touched experts spread over the touched set (each on the tokens
+    routed to it), and the call is estimated as sort (in full) + activation encoding (on up to 512
+    token rows, scaled to all tokens) + touched x dequantization + routed rows x per-row time.
+    Returns (µs per call, sampled experts, touched experts)."""
     from oracle import moe as om
     from quantized_moe_expert_sort_amd import inputs as gen
     ids, w, x = problem["topk_ids"], problem["topk_w"], problem["x"]
     E, T = wl.experts, wl.tokens
-    touched = np.unique(ids[(ids >= 0) & (ids < E)])
+    local = (ids >= 0) & (ids < E)
+    touched = np.unique(ids[local])
     pick = np.unique(touched[np.linspace(0, len(touched) - 1, min(max_experts, len(touched))).round().astype(int)])
     w1, w1s, w2, w2s = weights_host
     t0 = time.perf_counter()
@@ -537,17 +541,23 @@ def cpu_oracle_call_us(wl, weights_host, problem, max_experts, budget_s):
     t0 = time.perf_counter()
     om.activation_values(x[:nx], wl.a_dtype)
     t_act = (time.perf_counter() - t0) * T / nx
-    t_fused, n = 0.0, 0
+    t_deq, t_rows, n_rows, n = 0.0, 0.0, 0, 0
     for e in pick:
         toks = np.nonzero((ids == e).any(axis=1))[0]
         t0 = time.perf_counter()
+        om.expert_weights(w1, w1s, w2, w2s, int(e))
+        t1 = time.perf_counter()
         om.moe_fused(x[toks], wl.a_dtype, w1[e:e + 1], w1s[e:e + 1], w2[e:e + 1], w2s[e:e + 1], ids[toks], w[toks],
                      int(e), 1, "situv2", gen.BETA, gen.LINEAR_BETA)
-        t_fused += time.perf_counter() - t0
+        t2 = time.perf_counter()
+        t_deq += t1 - t0
+        t_rows += max(0.0, (t2 - t1) - (t1 - t0))
+        n_rows += int((ids[toks] == e).sum())
         n += 1
-        if t_fused >= budget_s:
+        if t2 - t0 + t_deq >= budget_s:
             break
-    return (t_sort + t_act + t_fused * len(touched) / n) * 1e6, n, len(touched)
+    est = t_sort + t_act + len(touched) * t_deq / n + int(local.sum()) * t_rows / max(n_rows, 1)
+    return est * 1e6, n, len(touched)
 
 
 def cpu_baseline(wl, weights_host, problems, budget_s=12.0):
@@ -650,9 +660,9 @@ def main():
                 us, n, u = cpu_oracle_call_us(t, thost, tb.host[0], 4 if t.inter_dim > 1024 else 16, 2.0)
                 tiers[name]["cpu_oracle_us_per_call"] = round(us, 1)
                 tiers[name]["cpu_oracle_sample"] = (f"routing 0: sort in full, activation encoding on "
-                                                    f"{min(t.tokens, 512)} rows scaled to {t.tokens}, fused "
-                                                    f"operator on {n} of {u} touched experts (their routed "
-                                                    f"tokens) scaled x{u / n:.2f}")
+                                                    f"{min(t.tokens, 512)} rows scaled to {t.tokens}, per-expert "
+                                                    f"dequantization and per-row time from {n} of {u} touched "
+                                                    f"experts, scaled to {u} experts and all routed rows")
             log(f"{name}: {tiers[name]}")
             del tb
             torch.cuda.empty_cache()
