@@ -978,12 +978,17 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
 //
 // With a skewed routing a few experts are chosen by a large share of the tokens (the prefill
 // workload's Zipf prior: the top 16 experts hold ~64% of the routed rows).  Their Stage2 rows are
-// taken token-major: an item is 128 consecutive tokens x 256 output columns and loops over the hot
-// experts, gathering for each the intermediate rows of the item's tokens (the workspace's zero row
-// for a token that does not route to it), so the router-weighted contributions of all hot experts
-// to a token add up in registers and one bf16 partial row per token is stored, instead of one row
-// per (token, hot expert) that the combine would read back.  The other experts' groups take the
+// taken token-major: an item is 256 (fp4) or 128 (fp8) consecutive tokens x 256 output columns
+// and loops over the hot experts, gathering for each the intermediate rows of the item's tokens
+// (the workspace's zero row for a token that does not route to it), so the router-weighted
+// contributions of all hot experts to a token add up in registers and one bf16 partial row per
+// token is stored, instead of one row per (token, hot expert) that the combine would read back.  The other experts' groups take the
 // grouped Stage2 as before, and the combine adds the token's partial row to its other rows.
+// The router weights enter without a second set of accumulators: a token row's accumulator is
+// kept divided by s, the weight of the last hot expert the token routes to, so at the first K
+// step of expert e (weight w != 0) the accumulator is multiplied by s / w before the matrix
+// cores add W2[e] y, s becomes w, and the stored row is s times the accumulator.  A token that
+// does not route to e reads the zero row (adding exact zeros) and keeps its s.
 // An expert is hot when its rows are at least a quarter of the tokens (so at most a quarter of an
 // item's MFMA rows are zero rows), up to MOE_HOT_MAX experts in ascending expert order.
 
@@ -1028,11 +1033,13 @@ __global__ __launch_bounds__(TABLE_THREADS) void hot_table_kernel(FusedArgs p, i
 // weights (128 tokens x MOE_HOT_MAX each) and the hot experts.
 template <int ADT>
 struct HFmt {
-  static constexpr int BM = 128;                          // tokens per item
-  static constexpr int MF = BM / WM / 16;                 // 16-row fragments per wave: 4
+  // tokens per item: 256 with fp4 intermediates (each copied weight row serves twice the
+  // tokens), 128 with fp8 (the 256-row fp8 tile would leave LDS for one step in flight)
+  static constexpr int BM = ADT == DT_FP4 ? 256 : 128;
+  static constexpr int MF = BM / WM / 16;                 // 16-row fragments per wave: 8 or 4
   static constexpr int KA = ADT == DT_FP8 ? 128 : 64;     // A bytes per row per K step
   static constexpr int ACPR = KA / 16;
-  static constexpr int P = ADT == DT_FP4 ? 5 : 4;         // LDS buffers
+  static constexpr int P = ADT == DT_FP4 ? 3 : 4;         // LDS buffers
   static constexpr int A_BYTES = BM * KA;
   static constexpr int B_BYTES = BNW * 64;
   static constexpr int BUF = A_BYTES + B_BYTES + (BM + BNW) * 4;
@@ -1146,11 +1153,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
   int n_st = 0;
   for (; item < it_hi; item += stride) {
     const int nxt = item + stride;
-    v4f acc[MF][NFW], tmp[MF][NFW];
+    v4f acc[MF][NFW];
+    float sc[MF];                                         // the divisor of each row's accumulator
 #pragma unroll
-    for (int f = 0; f < MF; ++f)
+    for (int f = 0; f < MF; ++f) {
+      sc[f] = 1.f;
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) acc[f][j] = tmp[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NFW; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
 
     auto compute = [&](int buf) {
       const uint8_t* la = lds + buf * F::BUF;
@@ -1185,7 +1195,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
         uint32_t xs_nxt = xs_cur;
         if (f + 1 < MF) load_x(f + 1, x_nxt, xs_nxt);
 #pragma unroll
-        for (int j = 0; j < NFW; ++j) tmp[f][j] = mfma_w_x<ADT>(wop[j], x_cur, tmp[f][j], wsc[j], xs_cur);
+        for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xs_cur);
         __builtin_amdgcn_sched_barrier(0);
         x_cur = x_nxt;
         xs_cur = xs_nxt;
@@ -1195,20 +1205,22 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
     for (int ss = 0; ss < SS; ++ss) {
       wait_and_barrier(loader ? per_step * min(SS - 1 - ss, P - 2) + (ss < P - 1 ? n_st : 0) : 63);
       if (loader && ss + P - 1 < SS) issue(item, ss + P - 1, (ss + P - 1) % P);
-      compute(ss % P);
-      if ((ss + 1) % S == 0) {                             // the expert's last K step: weight and add
+      if (ss % S == 0) {                                   // the expert's first K step: rescale
         const int hh = ss / S;
 #pragma unroll
         for (int f = 0; f < MF; ++f) {
           const float wv = tw[(arow0 + 16 * f + r16) * HOT_MAX + hh];
+          if (wv != 0.f) {
+            const float r = sc[f] / wv;
 #pragma unroll
-          for (int j = 0; j < NFW; ++j) {
+            for (int j = 0; j < NFW; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[f][j][i] += wv * tmp[f][j][i];
-            tmp[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+              for (int i = 0; i < 4; ++i) acc[f][j][i] *= r;
+            sc[f] = wv;
           }
         }
       }
+      compute(ss % P);
     }
     lds_barrier();                                        // every operand and table read is done
     const int tok_base = (item % ntl) * BM;
@@ -1233,8 +1245,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
       uint32_t d[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        d[k] = (uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1)]) |
-               ((uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1) + 1]) << 16);
+        d[k] = (uint32_t)f32_to_bf16_rne(sc[f] * acc[f][k >> 1][2 * (k & 1)]) |
+               ((uint32_t)f32_to_bf16_rne(sc[f] * acc[f][k >> 1][2 * (k & 1) + 1]) << 16);
       if (tok < T) {
         uint8_t* o = p.hot_out + ((size_t)tok * D + (size_t)nb * BNW + 64 * wn + 8 * g) * 2;
         *reinterpret_cast<uint4*>(o) = uint4{d[0], d[1], d[2], d[3]};
