@@ -974,6 +974,283 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
   }
 }
 
+// ---------------------------------------------------------------- grouped Stage2, resident rows
+//
+// With the short K of a tensor-parallel shard (I = 384) a group's whole intermediate tile fits
+// in LDS (at most 96 KB: 256 rows x 384 fp8 or fp4 codes, 128 rows x 384 bf16), so an item takes
+// a range of up to RB consecutive column blocks instead of one: the loaders copy the A tile (every
+// K step, with its scale dwords) once, then stream the weight rows of the range through a ring of
+// P2 buffers, K step after K step and column block after column block without a break, and each
+// column block's output rows are stored as soon as its last K step is done.  Against one column
+// block per item this reads the group's intermediate rows RB times less often and keeps the copy
+// pipeline running between column blocks.  The arithmetic of an output element (operands, MFMA
+// order over K, rounding) is that of grouped_stage2_kernel.
+
+template <int ADT>
+struct RFmt {
+  using F = GFmt<ADT>;
+  static constexpr int S_MAX = 3;                                   // K steps of 128 kept in LDS
+  static constexpr int P2 = ADT == DT_FP4 ? 4 : 3;                  // weight buffers
+  static constexpr int AS_BYTES = ADT == DT_BF16 ? 0 : F::BM * 4;   // A scale dwords of a step
+  static constexpr int A_STEP = F::A_BYTES + AS_BYTES;
+  static constexpr int A_REGION = S_MAX * A_STEP;
+  static constexpr int B_BUF = F::B_BYTES + BNW * 4;                // weight rows + scale dwords
+  static constexpr int BYTES = A_REGION + P2 * B_BUF;
+  static constexpr int RB = 4;                                      // column blocks per item, at most
+  static constexpr int NB_STEP = F::B_IPL + 1;                      // copies per weight step per loader
+};
+
+bool resident_stage2(const FusedArgs& a) { return a.I % 128 == 0 && a.I / 128 <= RFmt<DT_FP8>::S_MAX; }
+
+template <int ADT>
+__global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedArgs p, const int2* __restrict__ groups,
+                                                                         const int32_t* __restrict__ num_groups,
+                                                                         int n_nblk, int n_rng) {
+  using F = GFmt<ADT>;
+  using R = RFmt<ADT>;
+  constexpr int KA = F::KA, ACPR = F::ACPR, BM = F::BM, MF = F::MF, P2 = R::P2;
+  constexpr bool HAS_AS = ADT != DT_BF16;
+  constexpr int PARTS = GT / F::GTA;
+  static_assert(R::BYTES <= 160 * 1024, "LDS");
+  static_assert((P2 - 2) * R::NB_STEP + (P2 - 1) * 2 * MF <= 62, "vmcnt wait counts fit");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[R::BYTES];
+
+  const int D = p.D, I = p.I;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wave-uniform
+  const bool loader = wave < NLOAD;
+  const int lw = wave & (NLOAD - 1);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+  const int S = I / 128;                                  // <= S_MAX (resident_stage2)
+  const uint32_t lds0 = lds_addr(lds);
+  const size_t a_rowbytes = (size_t)I * KA / 128;
+
+  const int ng = ld_const(num_groups);
+  const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
+  const int per_part = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_rng;   // items (part, group, column range)
+  const int items_here = PARTS * per_part;
+
+  // weight copies: loader lw's instruction i moves rows 16 j .. 16 j + 15 (j = i * NLOAD + lw) of a
+  // column block's K step, chunks XOR-swizzled as grouped_stage2_kernel reads them
+  uint32_t b_off[F::B_IPL];
+#pragma unroll
+  for (int i = 0; i < F::B_IPL; ++i) {
+    const int j = i * NLOAD + lw;
+    const int qq = j * WAVE + lane;
+    const int row = qq / 4, part = swz_slot<4>(row, qq % 4) - row * 4;
+    b_off[i] = (uint32_t)row * (uint32_t)(I / 2) + part * 16;
+  }
+  const int sc_row = lw * WAVE + lane;
+  const uint32_t bs_off = (uint32_t)sc_row * (uint32_t)(I / 32);
+  const int arow0 = 16 * wm;                              // fragments alternate between the wave rows
+
+  for (int local = local0; local < items_here; local += stride) {
+    const int part = local >= per_part ? 1 : 0, rem = local - part * per_part;
+    const int gl = rem / n_rng, rg = rem - gl * n_rng;
+    const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
+    int tile0 = ld_const(gp), ntiles = ld_const(gp + 1);
+    if (PARTS == 2) {
+      const int h0 = ntiles <= F::GTA ? ntiles : (ntiles + 1) >> 1;
+      tile0 += part ? h0 : 0;
+      ntiles = part ? ntiles - h0 : h0;
+    }
+    const int cb0 = rg * n_nblk / n_rng, cb1 = (rg + 1) * n_nblk / n_rng;
+    if (ntiles == 0 || cb0 == cb1) continue;             // the empty second part of a small group
+    const int rows_used = ntiles * 32, row_base = tile0 * 32;
+    const int e = ld_const(p.expert_ids + tile0);
+    const uint8_t* qa = p.inter + (size_t)row_base * a_rowbytes;
+    const uint8_t* qas = p.inter_s + (size_t)row_base * (I / 32);
+    const uint8_t* qb = p.w2 + (size_t)e * D * (I / 2);
+    const uint8_t* qbs = p.w2s + (size_t)e * D * (I / 32);
+    uint32_t a_off[F::A_IPL];
+    int n_ai = 0;
+#pragma unroll
+    for (int i = 0; i < F::A_IPL; ++i) {
+      const int j = i * NLOAD + lw;
+      const int qq = j * WAVE + lane;
+      const int row = qq / ACPR, pt = swz_slot<ACPR>(row, qq % ACPR) - row * ACPR;
+      a_off[i] = (uint32_t)(row < rows_used ? row : 0) * (uint32_t)a_rowbytes + pt * 16;
+      n_ai += j * F::ROWS_PER_AI < rows_used;
+    }
+    const bool as_on = HAS_AS && lw * WAVE < rows_used;
+    const uint32_t as_off = (uint32_t)(sc_row < rows_used ? sc_row : 0) * (uint32_t)(I / 32);
+    const int NT = (cb1 - cb0) * S;                       // weight steps of the item
+
+    // weight step t = (column block cb0 + t / S, K step t % S) into ring buffer t % P2
+    auto issue_b = [&](int t) {
+      const int c = t / S, s = t - c * S;
+      const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + R::A_REGION + (t % P2) * R::B_BUF);
+      const uint8_t* bb = qb + (size_t)(cb0 + c) * BNW * (I / 2) + s * 64;
+#pragma unroll
+      for (int i = 0; i < F::B_IPL; ++i) dma16(bb, b_off[i], L + (i * NLOAD + lw) * 1024);
+      dma4(qbs + (size_t)(cb0 + c) * BNW * (I / 32) + s * 4, bs_off, L + F::B_BYTES + lw * 256);
+    };
+
+    lds_barrier();                                        // every read of the previous item's tiles is done
+    if (loader) {
+      for (int s = 0; s < S; ++s) {
+        const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + s * R::A_STEP);
+        const uint8_t* ab = qa + s * KA;
+#pragma unroll
+        for (int i = 0; i < F::A_IPL; ++i)
+          if (i < n_ai) dma16(ab, a_off[i], L + (i * NLOAD + lw) * 1024);
+        if (as_on) dma4(qas + s * 4, as_off, L + F::A_BYTES + lw * 256);
+      }
+#pragma unroll
+      for (int t = 0; t < P2 - 1; ++t)
+        if (t < NT) issue_b(t);
+    }
+    const int n_af = max(0, min(MF, (rows_used - arow0 + 2 * 16 - 1) / (2 * 16)));
+
+    auto run = [&](auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+      v4f acc[NA > 0 ? NA : 1][NFW];
+
+      auto compute_bf16 = [&](const uint8_t* la, const uint8_t* lb) {
+        const uint32_t* lbs = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
+        v8bf wop[NFW][4];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          const int br = 64 * wn + (j >> 1) * 32 + 8 * (r16 >> 2) + 4 * (j & 1) + (r16 & 3);
+          const uint4 q = *reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16);
+          const float sc = e8m0_to_float((lbs[br] >> (8 * g)) & 0xFFu);
+          wop[j][0] = fp4x8_to_bf16(q.x, sc);
+          wop[j][1] = fp4x8_to_bf16(q.y, sc);
+          wop[j][2] = fp4x8_to_bf16(q.z, sc);
+          wop[j][3] = fp4x8_to_bf16(q.w, sc);
+        }
+        auto load_x = [&](int f, v8bf* x) {
+          const int ar = arow0 + 32 * f + r16;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint4 q = *reinterpret_cast<const uint4*>(la + swz_slot<16>(ar, 4 * g + jj) * 16);
+            x[jj] = as_bf16x8(q.x, q.y, q.z, q.w);
+          }
+        };
+        v8bf x_cur[4];
+        load_x(0, x_cur);
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+          v8bf x_nxt[4] = {x_cur[0], x_cur[1], x_cur[2], x_cur[3]};
+          if (f + 1 < NA) load_x(f + 1, x_nxt);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_bf16(wop[j][jj], x_cur[jj], acc[f][j]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) x_cur[jj] = x_nxt[jj];
+        }
+      };
+
+      auto compute_q = [&](const uint8_t* la, const uint8_t* lb) {
+        const uint32_t* las = reinterpret_cast<const uint32_t*>(la + F::A_BYTES);
+        const uint32_t* lbs = reinterpret_cast<const uint32_t*>(lb + F::B_BYTES);
+        v8i wop[NFW];
+        uint32_t wsc[NFW];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          const int br = 64 * wn + (j >> 1) * 32 + 8 * (r16 >> 2) + 4 * (j & 1) + (r16 & 3);
+          wop[j] = fp4_operand_lo(*reinterpret_cast<const uint4*>(lb + swz_slot<4>(br, g) * 16));
+          wsc[j] = (lbs[br] >> (8 * g)) & 0xFFu;
+        }
+        auto load_x = [&](int f, v8i& xop, uint32_t& xsc) {
+          const int ar = arow0 + 32 * f + r16;
+          if (ADT == DT_FP8) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, g) * 16);
+            const uint4 hi = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, 4 + g) * 16);
+            xop = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          } else {
+            xop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
+          }
+          xsc = (las[ar] >> (8 * g)) & 0xFFu;
+        };
+        v8i x_cur;
+        uint32_t xs_cur;
+        load_x(0, x_cur, xs_cur);
+#pragma unroll
+        for (int f = 0; f < NA; ++f) {
+          v8i x_nxt = x_cur;
+          uint32_t xs_nxt = xs_cur;
+          if (f + 1 < NA) load_x(f + 1, x_nxt, xs_nxt);
+#pragma unroll
+          for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xs_cur);
+          __builtin_amdgcn_sched_barrier(0);
+          x_cur = x_nxt;
+          xs_cur = xs_nxt;
+        }
+      };
+
+      for (int t = 0; t < NT; ++t) {
+        const int c = t / S, s = t - c * S;
+        // a loader's copies of step t are done once at most those issued after them remain: the
+        // copies of steps t+1 .. t+P2-2 and the stores of the column blocks that ended after
+        // step t's copies were issued (at iteration t-P2+1, or at the item's start)
+        int later = 0;
+        if (loader) {
+          const int hi = min(t + P2 - 2, NT - 1);
+          later = (hi > t ? hi - t : 0) * R::NB_STEP;
+          for (int i = max(0, t - P2 + 1); i < t; ++i)
+            if (i % S == S - 1) later += 2 * NA;
+        }
+        wait_and_barrier(loader ? later : 63);
+        if (loader && t + P2 - 1 < NT) issue_b(t + P2 - 1);   // refills the buffer of step t-1
+        if (s == 0) {
+#pragma unroll
+          for (int f = 0; f < NA; ++f)
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        if (NA > 0) {
+          const uint8_t* la = lds + s * R::A_STEP;
+          const uint8_t* lb = lds + R::A_REGION + (t % P2) * R::B_BUF;
+          if constexpr (ADT == DT_BF16) compute_bf16(la, lb);
+          else compute_q(la, lb);
+        }
+        if (s == S - 1) {
+          // row arow0 + 32 f + r16, output columns 64 wn + 8 g .. + 7 and 64 wn + 32 + 8 g .. + 7
+          // of column block cb0 + c
+          uint8_t* obase =
+              p.rowout + (((size_t)row_base + arow0 + r16) * D + (size_t)(cb0 + c) * BNW + 64 * wn + 8 * g) * 2;
+#pragma unroll
+          for (int f = 0; f < NA; ++f) {
+            uint32_t d[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              d[k] = (uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1)]) |
+                     ((uint32_t)f32_to_bf16_rne(acc[f][k >> 1][2 * (k & 1) + 1]) << 16);
+            uint8_t* o = obase + (size_t)32 * f * D * 2;
+            *reinterpret_cast<uint4*>(o) = uint4{d[0], d[1], d[2], d[3]};
+            *reinterpret_cast<uint4*>(o + 64) = uint4{d[4], d[5], d[6], d[7]};
+          }
+        }
+      }
+    };
+    if constexpr (MF == 4) {
+      switch (n_af) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
+      }
+    } else {
+      switch (n_af) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 5: run(std::integral_constant<int, 5>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        case 7: run(std::integral_constant<int, 7>{}); break;
+        default: run(std::integral_constant<int, 8>{}); break;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- token-major Stage2 of hot experts
 //
 // With a skewed routing a few experts are chosen by a large share of the tokens (the prefill
@@ -1282,7 +1559,12 @@ hipError_t launch_grouped_stage(const FusedArgs& a, const int2* groups, const in
         ngroups = a.num_cgroups;
       }
     }
-    grouped_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+    if (resident_stage2(a)) {
+      const int n_rng = (n_nblk + RFmt<ADT>::RB - 1) / RFmt<ADT>::RB;
+      grouped_stage2_res_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk, n_rng);
+    } else {
+      grouped_stage2_kernel<ADT><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
+    }
   } else if (a.act == ACT_SITUV2)
     grouped_stage1_kernel<ADT, ACT_SITUV2><<<grid, GTHREADS, 0, s>>>(a, groups, ngroups, n_nblk);
   else
