@@ -996,7 +996,7 @@ struct RFmt {
   static constexpr int A_REGION = S_MAX * A_STEP;
   static constexpr int B_BUF = F::B_BYTES + BNW * 4;                // weight rows + scale dwords
   static constexpr int BYTES = A_REGION + P2 * B_BUF;
-  static constexpr int RB = 4;                                      // column blocks per item, at most
+  static constexpr int RB = 7;                                      // column blocks per item, at most
   static constexpr int NB_STEP = F::B_IPL + 1;                      // copies per weight step per loader
 };
 
