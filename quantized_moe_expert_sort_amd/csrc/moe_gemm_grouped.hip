@@ -57,23 +57,23 @@ static_assert(WM * WN == GWAVES, "wave grid");
 // ---------------------------------------------------------------- tile groups
 //
 // groups[g] = (first tile, tile count).  The tiles of an expert (a maximal run of equal
-// expert_ids; the sort writes them in ascending expert order) are cut into ceil(n / GT) groups
-// of ceil(n / ceil(n / GT)) tiles (the last one shorter).  One workgroup of 1024 threads: the
-// tile -> expert map is staged in LDS (up to GROUP_LDS_TILES tiles, else read from global
-// memory), each thread owns a contiguous chunk of tiles and finds the bounds of a run by binary
-// search (once per expert it meets), and a workgroup scan of the per-chunk group counts places
-// the groups in tile order.
+// expert_ids; the sort writes them in ascending expert order, so there are at most
+// MOE_SORT_MAX_EXPERTS runs) are cut into groups of gs = ceil(n / ceil(n / GT)) tiles (the last
+// one shorter).  One workgroup of 1024 threads, in three passes with a workgroup scan after each
+// of the first two: (1) each thread counts the run starts (a tile whose expert differs from the
+// previous tile's) in its contiguous chunk of tiles and records their positions in LDS; (2) each
+// thread takes a contiguous chunk of runs and derives their group and hot counts, which the
+// scans turn into output positions; (3) each thread writes the hot index of every tile of its
+// tile chunk.  The tile -> expert map is staged in LDS (up to GROUP_LDS_TILES tiles, else read
+// from global memory).
 
 constexpr int GROUP_THREADS = 1024;
 constexpr int GROUP_LDS_TILES = 16384;
+constexpr int GROUP_MAX_RUNS = MOE_SORT_MAX_EXPERTS;
 constexpr int HOT_MAX_G = MOE_HOT_MAX;
 
-__device__ __forceinline__ int group_size(int len) {
-  const int ng = (len + GT - 1) / GT;
-  return (len + ng - 1) / ng;
-}
-
 static_assert(GROUP_LDS_TILES % GROUP_THREADS == 0, "whole loads per thread");
+static_assert(GROUP_MAX_RUNS % GROUP_THREADS == 0, "whole runs per thread");
 // Besides the groups, the same passes pick the hot experts of the token-major Stage2 (below): an
 // expert whose run has at least hot_min_tiles tiles is hot, hot indices follow the expert order
 // up to MOE_HOT_MAX; every tile gets its expert's hot index (or -1) in tile_hot, the hot experts
@@ -88,7 +88,9 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __r
                                                               int32_t* __restrict__ tile_hot,
                                                               int32_t* __restrict__ hot_e) {
   __shared__ int lds_e[GROUP_LDS_TILES];
-  __shared__ int tmp[3][GROUP_THREADS / WAVE + 1];
+  __shared__ int run_start[GROUP_MAX_RUNS + 1];
+  __shared__ int run_hot[GROUP_MAX_RUNS];
+  __shared__ int tmp[2][GROUP_THREADS / WAVE + 1];
   const int n = min(*num_tiles_p, cap);
   const bool in_lds = n <= GROUP_LDS_TILES;
   if (in_lds) {   // GROUP_LDS_TILES / GROUP_THREADS loads per thread, all issued before the stores
@@ -106,118 +108,116 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __r
     }
   }
   __syncthreads();
-  // the tile -> expert reads of the searches: one instantiation reads LDS, the other global
-  // memory (a select between the two would become a generic-address load on every step)
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  // exclusive scans of two per-thread counts over the workgroup; also the totals
+  auto scan2 = [&](int v0, int v1, int (&ex)[2], int (&tot)[2]) {
+    int vv[2] = {v0, v1};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int sc = vv[q];
+#pragma unroll
+      for (int d = 1; d < WAVE; d <<= 1) {
+        const int o = __shfl_up(sc, d, WAVE);
+        if (lane >= d) sc += o;
+      }
+      if (lane == WAVE - 1) tmp[q][w] = sc;
+      vv[q] = sc;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      int run = 0;
+      for (int i = 0; i < GROUP_THREADS / WAVE; ++i) { const int c = tmp[threadIdx.x][i]; tmp[threadIdx.x][i] = run; run += c; }
+      tmp[threadIdx.x][GROUP_THREADS / WAVE] = run;
+    }
+    __syncthreads();
+    ex[0] = tmp[0][w] + vv[0] - v0;
+    ex[1] = tmp[1][w] + vv[1] - v1;
+    tot[0] = tmp[0][GROUP_THREADS / WAVE];
+    tot[1] = tmp[1][GROUP_THREADS / WAVE];
+    __syncthreads();
+  };
+  // the tile -> expert reads: one instantiation reads LDS, the other global memory (a select
+  // between the two would become a generic-address load on every read)
   auto work = [&](auto E) {
     const int per = (n + GROUP_THREADS - 1) / GROUP_THREADS;
     const int t0 = min(n, (int)threadIdx.x * per), t1 = min(n, t0 + per);
-    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-
-    // run bounds [rs, re) of tile t's expert e = E(t), found by galloping outwards from t (steps
-    // 1, 2, 4, ...) and then bisecting the last step: a run of length r costs ~2 log2(r) reads,
-    // so the many one-tile experts of a skewed routing cost one read per bound
-    auto run_start = [&](int t, int e) {
-      int hi = t, lo = t - 1;                             // E(hi) == e
-      for (int d = 1; lo >= 0 && E(lo) == e; d <<= 1) { hi = lo; lo = hi - 2 * d; }
-      lo = max(lo, -1);                                   // lo == -1 or E(lo) != e
-      while (hi - lo > 1) { const int m = (lo + hi) >> 1; if (E(m) == e) hi = m; else lo = m; }
-      return hi;
-    };
-    auto run_end = [&](int t, int e) {
-      int lo = t, hi = t + 1;                             // E(lo) == e
-      for (int d = 1; hi < n && E(hi) == e; d <<= 1) { lo = hi; hi = lo + 2 * d; }
-      hi = min(hi, n);                                    // hi == n or E(hi) != e
-      while (hi - lo > 1) { const int m = (lo + hi) >> 1; if (E(m) == e) lo = m; else hi = m; }
-      return hi;
-    };
-    // cached while consecutive tiles share the expert; a new expert inside the chunk starts at t
-    int cur_e = INT32_MIN, rs = 0, re = 0;
-    auto bounds = [&](int t) {
-      const int e = E(t);
-      if (e == cur_e) return;
-      rs = cur_e == INT32_MIN ? run_start(t, e) : t;
-      cur_e = e;
-      re = run_end(t, e);
-    };
-    // pass 1: groups, hot runs starting here, groups of the runs that are not hot
-    int starts = 0, hot_here = 0;
-    for (int t = t0; t < t1; ++t) {
-      bounds(t);
-      starts += ((t - rs) % group_size(re - rs)) == 0;
-      hot_here += t == rs && re - rs >= hot_min_tiles;
-    }
-    // exclusive scans of the three counts over the workgroup (cold groups: after hot indices)
-    auto scan3 = [&](int v0, int v1, int (&ex)[2], int (&tot)[2]) {
-      int vv[2] = {v0, v1};
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        int sc = vv[q];
-#pragma unroll
-        for (int d = 1; d < WAVE; d <<= 1) {
-          const int o = __shfl_up(sc, d, WAVE);
-          if (lane >= d) sc += o;
-        }
-        if (lane == WAVE - 1) tmp[q][w] = sc;
-        vv[q] = sc;
-      }
-      __syncthreads();
-      if (threadIdx.x < 2) {
-        int run = 0;
-        for (int i = 0; i < GROUP_THREADS / WAVE; ++i) { const int c = tmp[threadIdx.x][i]; tmp[threadIdx.x][i] = run; run += c; }
-        tmp[threadIdx.x][GROUP_THREADS / WAVE] = run;
-      }
-      __syncthreads();
-      ex[0] = tmp[0][w] + vv[0] - v0;
-      ex[1] = tmp[1][w] + vv[1] - v1;
-      tot[0] = tmp[0][GROUP_THREADS / WAVE];
-      tot[1] = tmp[1][GROUP_THREADS / WAVE];
-      __syncthreads();
-    };
+    auto is_start = [&](int t) { return t == 0 || E(t) != E(t - 1); };
+    // (1) run starts: positions in tile order
+    int starts = 0;
+    for (int t = t0; t < t1; ++t) starts += is_start(t);
     int ex[2], tot[2];
-    scan3(starts, hot_here, ex, tot);
-    const int hbase = ex[1];
-    const int nh = min(tot[1], HOT_MAX_G);
-    // the hot index of tile t's run: runs starting in this chunk count from hbase, a run that
-    // started before the chunk is the last hot run before it
-    auto hot_index = [&](int t, int h_next) {
-      if (re - rs < hot_min_tiles) return -1;
-      const int h = rs >= t0 ? h_next : hbase - 1;
-      return h < HOT_MAX_G ? h : -1;
-    };
-    int cold_here = 0;
-    cur_e = INT32_MIN;
+    scan2(starts, 0, ex, tot);
+    const int rbase = ex[0];
+    const int nruns = min(tot[0], GROUP_MAX_RUNS);      // ascending expert ids: at most that many
     {
-      int hn = hbase;
-      for (int t = t0; t < t1; ++t) {
-        bounds(t);
-        const int h = hot_index(t, t == rs ? hn : hn - 1);
-        if (t == rs && re - rs >= hot_min_tiles) ++hn;
-        cold_here += h < 0 && ((t - rs) % group_size(re - rs)) == 0;
+      int r = rbase;
+      for (int t = t0; t < t1; ++t)
+        if (is_start(t)) {
+          if (r < GROUP_MAX_RUNS) run_start[r] = t;
+          ++r;
+        }
+    }
+    if (threadIdx.x == 0) run_start[nruns] = n;
+    __syncthreads();
+    // (2) runs [r0, r1) of this thread: group counts and hot runs, then the cold group counts
+    constexpr int RPT = GROUP_MAX_RUNS / GROUP_THREADS;
+    const int rper = (nruns + GROUP_THREADS - 1) / GROUP_THREADS;   // <= RPT
+    const int r0 = min(nruns, (int)threadIdx.x * rper), r1 = min(nruns, r0 + rper);
+    int rs[RPT], len[RPT], gs[RPT], ng[RPT];
+    int my_groups = 0, my_hot = 0;
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      const int r = r0 + q;
+      rs[q] = r < r1 ? run_start[r] : 0;
+      len[q] = r < r1 ? run_start[r + 1] - rs[q] : 0;
+      const int parts = (len[q] + GT - 1) / GT;
+      gs[q] = parts > 0 ? (len[q] + parts - 1) / parts : 1;
+      ng[q] = (len[q] + gs[q] - 1) / gs[q];
+      my_groups += ng[q];
+      my_hot += len[q] > 0 && len[q] >= hot_min_tiles;
+    }
+    scan2(my_groups, my_hot, ex, tot);
+    const int nh = min(tot[1], HOT_MAX_G);
+    int hq[RPT], my_cold = 0;
+    {
+      int h = ex[1];
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const bool hot = len[q] > 0 && len[q] >= hot_min_tiles;
+        hq[q] = hot && h < HOT_MAX_G ? h : -1;
+        h += hot;
+        my_cold += hq[q] < 0 ? ng[q] : 0;
       }
     }
-    int ex2[2], tot2[2];
-    scan3(cold_here, 0, ex2, tot2);
-    int gidx = ex[0], cidx = ex2[0], hn = hbase;
-    cur_e = INT32_MIN;
-    for (int t = t0; t < t1; ++t) {
-      bounds(t);
-      const bool start_run = t == rs && re - rs >= hot_min_tiles;
-      const int h = hot_index(t, t == rs ? hn : hn - 1);
-      if (start_run) {
-        if (hn < HOT_MAX_G) hot_e[hn] = cur_e;
-        ++hn;
+    int exc[2], totc[2];
+    scan2(my_cold, 0, exc, totc);
+    {
+      int gidx = ex[0], cidx = exc[0];
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const int r = r0 + q;
+        if (r >= r1) break;
+        run_hot[r] = hq[q];
+        if (hq[q] >= 0) hot_e[hq[q]] = E(rs[q]);
+        for (int j = 0; j < ng[q]; ++j) {
+          const int2 gr = int2{rs[q] + j * gs[q], min(gs[q], len[q] - j * gs[q])};
+          groups[gidx++] = gr;
+          if (hq[q] < 0) cgroups[cidx++] = gr;
+        }
       }
-      tile_hot[t] = h;
-      const int gs = group_size(re - rs);
-      if ((t - rs) % gs == 0) {
-        const int2 gr = int2{t, min(gs, re - t)};
-        groups[gidx++] = gr;
-        if (h < 0) cgroups[cidx++] = gr;
+    }
+    __syncthreads();
+    // (3) the hot index of every tile: its run is the last run starting at or before it
+    {
+      int r = rbase - 1;
+      for (int t = t0; t < t1; ++t) {
+        r += is_start(t);
+        tile_hot[t] = r >= 0 && r < nruns ? run_hot[r] : -1;
       }
     }
     if (threadIdx.x == 0) {
       *num_groups = tot[0];
-      *num_cgroups = tot2[0];
+      *num_cgroups = totc[0];
       hot_e[HOT_MAX_G] = nh;
     }
   };
