@@ -21,12 +21,18 @@ constexpr int NWAVES = ITEM_WAVES;
 
 // ---------------------------------------------------------------- Stage1
 
+// Workgroup b runs on XCD b % 8 (workgroups are dealt to the eight XCDs round robin).  With
+// r = b / 8, it takes column block r % n_nblk of tile (r / n_nblk) * 8 + b % 8: the column blocks
+// of a tile are consecutive workgroups of one XCD, so the tile's gathered activation rows are
+// fetched into one L2 and re-read from there.  The grid covers cap_tiles rounded up to 8.
 template <int ADT, int BM, int NI, int KW, int PF, int MINW, int ACT, bool LDSA>
 __global__ __launch_bounds__(KW * WAVE, MINW) void stage1_kernel(FusedArgs p, int n_nblk) {
   __shared__ float red[KW][BM][2 * NI + 1];
   __shared__ __attribute__((aligned(16))) uint8_t astage[LDSA ? KW * AStage<ADT, PF>::BYTES : 16];
-  const int tile = blockIdx.x / n_nblk;
-  const int nb = blockIdx.x - tile * n_nblk;
+  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3;
+  const int tq = r / n_nblk;
+  const int tile = tq * 8 + xcd, nb = r - tq * n_nblk;
+  if (tile >= p.cap_tiles) return;
   stage1_item<ADT, BM, NI, KW, PF, ACT, false, LDSA>(p, tile, nb, red, astage);
 }
 
@@ -121,140 +127,213 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
 //
 // For at most SMALL_ROWS routed rows (decode), one kernel does Stage2 and the combine: workgroup
 // nb owns output columns [16 nb, 16 nb + 16) of every token.  Its sixteen waves take the layout's
-// tiles round robin (a non-empty expert has at least one row per tile, so at most SMALL_ROWS
-// tiles are in use and a wave has at most two; their expert ids are read together, and the
-// tiles past num_tiles carry expert -1, so num_tiles itself is never waited for); for each
-// tile a wave computes the 16 x 16 block (tile rows x the block's
-// columns) with exactly the MFMA sequence of stage2_item (same operands, K steps ascending),
-// scales it by the router weight and rounds it to bf16 as stage2_item stores it, into slot
-// [t*topk + k] of an LDS array.  The token sums then run
-// over k ascending with 0 for non-local rows, as the combine kernel does: the output has the
-// same bits as Stage2 + combine, without the per-row buffer or the extra launch.
+// tiles round robin, TPW tiles each (a non-empty expert has at least one routed row per tile, so
+// at most T*topk tiles are in use; tiles past num_tiles carry expert -1, so num_tiles itself is
+// never read).  A wave issues all of its memory traffic before its first MFMA: it copies the
+// intermediate rows of its tiles' routed rows into LDS (one slot per flat row index t*topk + k,
+// written and read by this wave only) and loads the weight bytes and scales of all its tiles into
+// registers, for SMALL_PS K steps at a time.  For each tile it then computes the 16 x 16 block
+// (tile rows x the block's columns) with the MFMA sequence of stage2_item (same operands, K steps
+// ascending) and keeps the fp32 sums in LDS.  The token sums run over k ascending: each routed
+// row's sum times its router weight, rounded to bf16 as stage2_item stores it, and nothing for
+// rows of non-local experts, as the combine kernel adds them: the output has the same bits as
+// Stage2 + combine, without the per-row buffer or the extra launch.
 
-// A wave walks its tiles one at a time, which loses to Stage2 + combine once it has several.
 constexpr int SMALL_ROWS = 32;
-constexpr int SMALL_THREADS = 1024;
-constexpr int SMALL_WAVES = SMALL_THREADS / WAVE;
-constexpr int SMALL_TPW = SMALL_ROWS / SMALL_WAVES;   // tiles per wave
-static_assert(SMALL_ROWS % SMALL_WAVES == 0, "every tile in use belongs to one wave");
+constexpr int SMALL_PS = 3;                           // K steps per pass (inter_dim 384: one pass)
 
-template <int ADT, int BM, int PF>
-__global__ __launch_bounds__(SMALL_THREADS) void stage2_small_kernel(FusedArgs p) {
+// wait_vm<STEP * n> for a wave-uniform n in [0, 1] (the loads of n later tiles still in flight)
+template <int STEP>
+__device__ __forceinline__ void wait_vm_n(int n) {
+  if (n == 0) wait_vm<0>();
+  else wait_vm<STEP>();
+}
+
+// s_barrier without the vector-memory wait that __syncthreads adds (loads stay in flight)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+// NW waves of TPW tiles each (16 x 1 or 16 x 2).  More rows per workgroup measured slower than
+// the per-tile Stage2 + combine: at 64 routed rows (dec-4) 16 x 4 took 17.8 us and 8 x 8 20.6 us
+// against 15.9 (each workgroup then streams 16-column slices of 64 experts' weights).
+template <int ADT, int BM, int NW, int TPW>
+__global__ __launch_bounds__(NW * WAVE) void stage2_small_kernel(FusedArgs p) {
+  static_assert(TPW <= 2, "wait_vm_n covers two tiles per wave");
   constexpr int MF = BM / 16;
-  __shared__ float vals[SMALL_ROWS][16];
+  constexpr int SMALL_WAVES = NW, SMALL_THREADS = NW * WAVE;
+  constexpr int NR = SMALL_WAVES * TPW;                                    // rows handled
+  constexpr int SB = 128 * row_bytes_num<ADT>() / row_bytes_den<ADT>();   // bytes of one K step
+  constexpr int SLOT = SMALL_PS * SB;
+  static_assert(SLOT % 16 == 0 && SLOT <= 16 * WAVE, "a row's pass is one copy instruction");
+  __shared__ float vals[NR][16];
+  __shared__ float wsh[NR];
+  __shared__ int written[NR];
+  __shared__ __attribute__((aligned(16))) uint8_t arows[NR * SLOT + SB];   // + one zero step
   const int nb = blockIdx.x;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / WAVE);   // wave-uniform
   const int r16 = lane & 15, g = lane >> 4;
   const int TK = p.T * p.topk, D = p.D, I = p.I, S = I / 128;
-  for (int i = threadIdx.x; i < TK * 16; i += SMALL_THREADS) (&vals[0][0])[i] = 0.f;
-  __syncthreads();
+  uint8_t* const zero_step = arows + NR * SLOT;
 
-  const size_t a_row = (size_t)I * row_bytes_num<ADT>() / row_bytes_den<ADT>();
+  // router weight of routed row threadIdx.x: requested first, needed only for the token sums
+  const float wmine = (int)threadIdx.x < TK ? p.topk_w[threadIdx.x] : 0.f;
   // expert ids and row ids of every tile of this wave, requested together
-  int eid[SMALL_TPW], vrq[SMALL_TPW][MF], vrowq[SMALL_TPW][MF][4];
+  int eid[TPW], vr[TPW][MF];
 #pragma unroll
-  for (int q = 0; q < SMALL_TPW; ++q) {   // unconditional loads (a tile past cap reads the last)
+  for (int q = 0; q < TPW; ++q) {   // unconditional loads (a tile past cap reads the last)
     const int tile = min(wave + SMALL_WAVES * q, p.cap_tiles - 1);
     eid[q] = p.expert_ids[tile];
 #pragma unroll
-    for (int f = 0; f < MF; ++f) {
-      vrq[q][f] = p.sorted_ids[tile * BM + 16 * f + r16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vrowq[q][f][i] = p.sorted_ids[tile * BM + 16 * f + 4 * g + i];
-    }
+    for (int f = 0; f < MF; ++f) vr[q][f] = p.sorted_ids[tile * BM + 16 * f + r16];
   }
+  if ((int)threadIdx.x < NR) written[threadIdx.x] = 0;
+  if ((int)threadIdx.x < SB / 4) reinterpret_cast<uint32_t*>(zero_step)[threadIdx.x] = 0u;
+  lds_barrier();
+
+  bool tv[TPW];   // wave-uniform: the tile has a local expert
+  int ew[TPW];    // its expert, or expert 0 (whose rows then serve as in-bounds stand-ins)
 #pragma unroll
-  for (int q = 0; q < SMALL_TPW; ++q)
-    if (wave + SMALL_WAVES * q >= p.cap_tiles) eid[q] = -1;
-#pragma unroll
-  for (int q = 0; q < SMALL_TPW; ++q) {
+  for (int q = 0; q < TPW; ++q) {
     const int tile = wave + SMALL_WAVES * q;
-    const int e = eid[q];
-    if (e < 0 || e >= p.E) continue;
-    int vr[MF], vrow[MF][4];
+    const int e = __builtin_amdgcn_readfirstlane(eid[q]);
+    tv[q] = tile < p.cap_tiles && e >= 0 && e < p.E;
+    ew[q] = tv[q] ? e : 0;
+  }
+  const size_t a_row = (size_t)I * row_bytes_num<ADT>() / row_bytes_den<ADT>();
+  const uint32_t lds_rows = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)arows);
+  v4f acc[TPW][MF];
 #pragma unroll
-    for (int f = 0; f < MF; ++f) {
-      vr[f] = vrq[q][f];
+  for (int q = 0; q < TPW; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vrow[f][i] = vrowq[q][f][i];
+    for (int f = 0; f < MF; ++f) acc[q][f] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto pass = [&](int s0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const int n_s = FULL ? SMALL_PS : S - s0;
+    // intermediate rows: one copy per routed row, lanes [0, n_s * SB / 16) of the wave
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      if (!tv[q]) continue;
+      const int tile = wave + SMALL_WAVES * q;
+#pragma unroll
+      for (int f = 0; f < MF; ++f) {
+        uint64_t m = __ballot((unsigned)vr[q][f] < (unsigned)TK) & 0xFFFFull;   // lanes 0..15: rows 0..15
+        while (m) {
+          const int l = __ffsll((unsigned long long)m) - 1;
+          m &= m - 1ull;
+          const int v = __builtin_amdgcn_readlane(vr[q][f], l);
+          const uint32_t off = (uint32_t)((size_t)(tile * BM + 16 * f + l) * a_row) + (uint32_t)(s0 * SB + 16 * lane);
+          if (lane < n_s * SB / 16) dma16_lds(p.inter, off, lds_rows + (uint32_t)(v * SLOT));
+        }
+      }
     }
-    // router weights of the accumulator rows, requested with the operands
-    float wv[MF][4];
+    // scales, then the weights of every tile slot and step, tile after tile; a slot without a
+    // local expert loads expert 0's bytes (the same lines for every such slot, served by the L2)
+    // so that every wave issues the same loads and a tile's wait below is a fixed count
+    ScaleQuads<SMALL_PS> bsq[TPW];
+    ScaleQuads<SMALL_PS> asq[TPW][MF];
+    uint4 bq[TPW][SMALL_PS];
 #pragma unroll
-    for (int f = 0; f < MF; ++f)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wv[f][i] = (unsigned)vrow[f][i] < (unsigned)TK ? p.topk_w[vrow[f][i]] : 0.f;
-    const uint8_t* arow[MF];
-    const uint8_t* asrow[MF];
-    bool aval[MF];
-#pragma unroll
-    for (int f = 0; f < MF; ++f) {
-      const size_t R = (size_t)tile * BM + 16 * f + r16;
-      aval[f] = (unsigned)vr[f] < (unsigned)TK;
-      arow[f] = p.inter + R * a_row;
-      asrow[f] = ADT == DT_BF16 ? nullptr : p.inter_s + R * (I / 32);
-    }
-    const size_t wr = (size_t)e * D + nb * 16 + r16;
-    const uint8_t* brow = p.w2 + wr * (I / 2);
-    const uint8_t* bsrow = p.w2s + wr * (I / 32);
-    v4f acc[MF];
-#pragma unroll
-    for (int f = 0; f < MF; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-    // scales and intermediate rows first, weights last: the MFMAs of step i wait only for the
-    // weights of steps <= i (loads complete in order)
-    auto chunk = [&](int s0, auto full) {
-      constexpr bool FULL = decltype(full)::value;
-      uint4 bq[PF];
-      ScaleQuads<PF> bsq;
-      AOperand<ADT> A[PF][MF];
-      ScaleQuads<PF> asq[MF];
-      bsq.load(bsrow, s0, S, g, true);
+    for (int q = 0; q < TPW; ++q) {
+      const size_t wr = (size_t)ew[q] * D + nb * 16 + r16;
+      bsq[q].load(p.w2s + wr * (I / 32), s0, s0 + n_s, g, tv[q]);
 #pragma unroll
       for (int f = 0; f < MF; ++f)
-        if (ADT != DT_BF16) asq[f].load(asrow[f], s0, S, g, aval[f]);
+        if (ADT != DT_BF16) {
+          const size_t R = (size_t)(wave + SMALL_WAVES * q) * BM + 16 * f + r16;
+          asq[q][f].load(p.inter_s + R * (I / 32), s0, s0 + n_s, g, tv[q] && (unsigned)vr[q][f] < (unsigned)TK);
+        }
+    }
 #pragma unroll
-      for (int i = 0; i < PF; ++i)
-        if (FULL || s0 + i < S)
+    for (int q = 0; q < TPW; ++q) {
+      const uint8_t* brow = p.w2 + ((size_t)ew[q] * D + nb * 16 + r16) * (I / 2) + 16 * g;
 #pragma unroll
-          for (int f = 0; f < MF; ++f) A[i][f].load(arow[f], s0 + i, g, aval[f]);
+      for (int i = 0; i < SMALL_PS; ++i)
+        if (FULL || i < n_s) bq[q][i] = ld16(brow + (s0 + i) * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto tile_mfmas = [&](int q) {
+      const uint8_t* abase[MF];
+      int astep[MF];
 #pragma unroll
-      for (int i = 0; i < PF; ++i)
-        if (FULL || s0 + i < S) bq[i] = ld16(brow + (s0 + i) * 64 + 16 * g);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int f = 0; f < MF; ++f) {
+        const int v = vr[q][f];
+        const bool in = (unsigned)v < (unsigned)TK;
+        abase[f] = in ? arows + v * SLOT : zero_step;
+        astep[f] = in ? SB : 0;
+      }
 #pragma unroll
-      for (int i = 0; i < PF; ++i) {
-        if (FULL || s0 + i < S) {
-          const uint32_t bs = bsq.get(i, r16, g);
+      for (int i = 0; i < SMALL_PS; ++i) {
+        if (FULL || i < n_s) {
+          const uint32_t bs = bsq[q].get(i, r16, g);
 #pragma unroll
           for (int f = 0; f < MF; ++f) {
-            const uint32_t as = ADT == DT_BF16 ? 0u : asq[f].get(i, r16, g);
-            acc[f] = A[i][f].mma(bq[i], bs, as, acc[f]);
+            AOperand<ADT> A;
+            A.load_lds(abase[f] + i * astep[f], g);
+            const uint32_t as = ADT == DT_BF16 ? 0u : asq[q][f].get(i, r16, g);
+            acc[q][f] = A.mma(bq[q][i], bs, as, acc[q][f]);
           }
         }
       }
     };
-    int s0 = 0;
-    for (; s0 + PF <= S; s0 += PF) chunk(s0, std::true_type{});
-    if (s0 < S) chunk(s0, std::false_type{});
+    // loads complete in order: once at most the later tiles' weight loads are outstanding, the
+    // copies, the scales and this tile's weights have arrived
+    if constexpr (FULL) {
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        wait_vm_n<SMALL_PS>(TPW - 1 - q);
+        if (tv[q]) tile_mfmas(q);
+      }
+    } else {
+      wait_vm<0>();
+#pragma unroll
+      for (int q = 0; q < TPW; ++q)
+        if (tv[q]) tile_mfmas(q);
+    }
+    // every LDS read of this pass is done before the next pass's copies replace the rows
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  int s0 = 0;
+  for (; s0 + SMALL_PS <= S; s0 += SMALL_PS) pass(s0, std::true_type{});
+  if (s0 < S) pass(s0, std::false_type{});
+
+  // fp32 sums of the routed rows: element i of lane (r16, g) is row 4 g + i of the fragment
+#pragma unroll
+  for (int q = 0; q < TPW; ++q)
 #pragma unroll
     for (int f = 0; f < MF; ++f)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int v = vrow[f][i];
-        if ((unsigned)v < (unsigned)TK) {
-          const float o = acc[f][i] * wv[f][i];
-          vals[v][r16] = __uint_as_float((uint32_t)f32_to_bf16_rne(o) << 16);
+        const int v = __shfl(vr[q][f], 4 * g + i, WAVE);
+        if (tv[q] && (unsigned)v < (unsigned)TK) {
+          vals[v][r16] = acc[q][f][i];
+          if (r16 == 0) written[v] = 1;
         }
       }
-  }
+  if ((int)threadIdx.x < TK) wsh[threadIdx.x] = wmine;
   __syncthreads();
   for (int idx = threadIdx.x; idx < p.T * 16; idx += SMALL_THREADS) {
     const int t = idx >> 4, c = idx & 15;
     float sum = 0.f;
-    for (int k = 0; k < p.topk; ++k) sum += vals[t * p.topk + k][c];
+    for (int k = 0; k < p.topk; ++k) {
+      const int v = t * p.topk + k;
+      if (written[v]) sum += __uint_as_float((uint32_t)f32_to_bf16_rne(vals[v][c] * wsh[v]) << 16);
+    }
     p.out[(size_t)t * D + nb * 16 + c] = f32_to_bf16_rne(sum);
   }
+}
+
+template <int ADT, int BM>
+hipError_t launch_stage2_small(const FusedArgs& a, hipStream_t s) {
+  const int rows = a.T * a.topk;
+  const dim3 grid((unsigned)(a.D / 16));
+  if (rows <= 16) stage2_small_kernel<ADT, BM, 16, 1><<<grid, 16 * WAVE, 0, s>>>(a);
+  else if (rows <= SMALL_ROWS) stage2_small_kernel<ADT, BM, 16, 2><<<grid, 16 * WAVE, 0, s>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // Stage tiling per activation dtype and block_m.
@@ -280,7 +359,7 @@ template <int ADT, int BM>
 hipError_t run_stages(FusedArgs a, hipStream_t s) {
   using C = Cfg<ADT, BM>;
   const int n1 = a.I / C::NI;
-  const unsigned grid1 = (unsigned)((int64_t)a.cap_tiles * n1);
+  const unsigned grid1 = (unsigned)((int64_t)(a.cap_tiles + 7) / 8 * 8 * n1);
   const int n2 = (a.D + NWAVES * C::NF2 * 16 - 1) / (NWAVES * C::NF2 * 16);
   constexpr int T1 = C::KW * WAVE;
   const bool tiled = tiled_path_supported(a);
@@ -311,10 +390,10 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   if (!(a.stages & 2) || a.act == ACT_NONE) return hipSuccess;
-  if ((int64_t)a.T * a.topk <= SMALL_ROWS && a.D % 16 == 0) {
-    stage2_small_kernel<ADT, BM, C::PF2><<<(unsigned)(a.D / 16), SMALL_THREADS, 0, s>>>(a);
-    return hipGetLastError();
-  }
+  // the small kernel's copies address the intermediate with 32-bit offsets
+  if ((int64_t)a.T * a.topk <= SMALL_ROWS && a.D % 16 == 0 &&
+      (int64_t)a.cap_tiles * BM * a.I * 2 < ((int64_t)1 << 31))
+    return launch_stage2_small<ADT, BM>(a, s);
   if (!tiled2) {
     const unsigned grid2 = (unsigned)((int64_t)a.cap_tiles * n2);
     // staged intermediate rows: the whole K in one chunk, 32-bit copy offsets

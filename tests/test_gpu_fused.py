@@ -84,6 +84,11 @@ SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
     (2, 64, 16, 512, 256, 0, 64, 32, "fp4", "situv2", 0.0),
     (4, 40, 8, 256, 384, 0, 40, 32, "bf16", "silu", 0.0),
     (8, 32, 4, 256, 256, 8, 8, 16, "fp8", "situv2", 0.0),        # expert-parallel shard
+    # 33..64 routed rows (per-tile Stage2 + combine); inter_dim 128 and 512
+    (4, 64, 16, 512, 256, 0, 64, 16, "bf16", "situv2", 0.0),
+    (3, 48, 16, 512, 384, 0, 48, 16, "fp8", "situv2", 0.0),
+    (5, 40, 12, 256, 128, 0, 40, 16, "fp4", "silu", 0.0),
+    (4, 32, 16, 256, 512, 8, 16, 16, "bf16", "situv2", 0.0),     # expert-parallel shard
     # >= 2048 tokens with model_dim % 512 == 0: the tiled large-batch
     # stages (Stage1 scale chunks span 4 K steps: 7 chunks at 3584, 2 at 1024, 1 at 512)
     (2048, 16, 4, 512, 256, 0, 16, 32, "fp8", "situv2", 1.1),

@@ -57,6 +57,10 @@ CASES = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act)
     (8, 32, 4, 512, 256, 0, 32, 16, "fp8", "situv2"),            # exactly 32 rows
     (2, 32, 16, 256, 128, 0, 32, 32, "fp4", "silu"),
     (6, 32, 4, 256, 256, 8, 8, 16, "fp4", "situv2"),            # expert-parallel: tokens w/o rows
+    # 33..64 routed rows at block_m 16 (per-tile Stage2 + combine)
+    (4, 64, 16, 512, 256, 0, 64, 16, "bf16", "situv2"),          # exactly 64 rows
+    (3, 40, 16, 256, 512, 0, 40, 16, "fp8", "situv2"),           # inter_dim 512
+    (4, 32, 12, 256, 128, 8, 16, 16, "fp4", "silu"),             # expert-parallel: tokens w/o rows
 ]
 
 
