@@ -9,7 +9,8 @@ is not served from the last-level cache.  Per workload it also measures:
 
 * each part alone over the same rotating routings (moe_fused over pre-sorted layouts, the sort,
   the quantization) and the two stage calls (Stage1; Stage2 + combine), timed with HIP events
-  on the stream the library launches on (torch's current stream);
+  on the stream the library launches on (torch's current stream), each timed pass preceded by
+  about 20 ms of untimed calls so that it measures the steady state;
 * moe_fused replayed from a HIP graph of N calls over the rotating layouts, median of 3;
 * the roofline of its dominant kernel: algorithmic bytes (HBM-bound workloads) or flops
   (MFMA-bound ones) per launch over that stage call's average time;
@@ -42,6 +43,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}   # dense; fp
 PAGES_US = {"dec-1": 28.3, "dec-4": 42.7, "dec-16": 107.3, "mid-64": 229.1, "mid-256": 329.8, "mid-1024": 365.7,
             "pre-a16-2048": 651.3, "pre-a16-4096": 1087.3, "pre-a16-8192": 1994.4, "pre-a16-16384": 3600.3,
             "pre-a8-8192": 1249.4}
+WARM_MS = 20.0   # untimed device work between the spin gate and each timed pass
 TIERS = ["dec-4", "dec-16", "mid-64", "mid-256", "mid-1024", "ep-8192", "pre-16384", "pre-a16-2048",
          "pre-a16-4096", "pre-a16-8192", "pre-a16-16384", "pre-a8-8192"]
 
@@ -153,11 +155,14 @@ class Workbench:
         self.qm.moe_fused(xa, xs, self.wl.a_dtype, *self.w, w, lay, self.wl.experts, "situv2", gen.BETA,
                           gen.LINEAR_BETA, out=self.out, ws=ws, stages=stages)
 
-    def device_ms(self, fn, steps, start):
+    def device_ms(self, fn, steps, start, warm_ms=WARM_MS):
         """Device time per call of fn(i), i = start .. start+steps-1.  The calls are enqueued behind
         a spin kernel so that the GPU runs them back to back (as under graph replay or any launcher
         that stays ahead of the device) rather than waiting on Python between launches; if the spin
-        ends before the host has enqueued everything, it is lengthened and the pass repeated."""
+        ends before the host has enqueued everything, it is lengthened and the pass repeated.
+        Untimed calls worth about warm_ms of device time run between the spin and the timed calls:
+        after the near-idle spin the heavy kernels run up to ~25% slower for the next ~10 ms (a
+        clock / power transient seen in kernel traces), which would otherwise be timed."""
         torch = self.torch
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         host = time.perf_counter()
@@ -165,11 +170,14 @@ class Workbench:
             fn(start + i)
         torch.cuda.synchronize()
         host_ms = (time.perf_counter() - host) * 1e3
-        spin_ms = max(5.0, 3.0 * host_ms)
+        warm = int(min(max(2, np.ceil(warm_ms * steps / max(host_ms, 1e-3))), 50 * steps))
+        spin_ms = max(5.0, 3.0 * host_ms * (warm + steps) / steps)
         for _ in range(4):
             gate = torch.cuda.Event()
             torch.cuda._sleep(int(spin_ms * self.cyc_per_ms))
             gate.record()
+            for i in range(warm):
+                fn(start - warm + i)
             t0.record()
             for i in range(steps):
                 fn(start + i)
