@@ -275,12 +275,16 @@ def is_hbm_bound(wl, r):
     return r["weight_bytes"] / (HBM_PEAK_GBPS * 1e9) >= r["flops"] / (MFMA_PEAK_TFLOPS[wl.a_dtype] * 1e12)
 
 
-# kernels behind each stage call, by path (the grouped large-batch path from 2048 tokens when
-# model_dim % 512 == 0; Stage2 and the combine in one kernel for at most 32 routed rows)
+# kernels behind each stage call, by path: the grouped large-batch path from 2048 tokens when
+# model_dim % 512 == 0 (with fp8 / fp4 activations the hot-expert table and token-major Stage2
+# are launched before the grouped Stage2, which keeps a group's rows in LDS up to inter_dim
+# 384); Stage2 and the combine in one kernel for at most 32 routed rows
 def stage_kernels(wl):
     grouped = wl.tokens >= 2048 and wl.block_m == 32 and wl.model_dim % 512 == 0
     if grouped:
-        return (["group_kernel", "grouped_stage1_kernel"], ["grouped_stage2_kernel", "combine_kernel"])
+        s2 = "grouped_stage2_res_kernel" if wl.inter_dim <= 384 else "grouped_stage2_kernel"
+        hot = ["hot_table_kernel", "hot_stage2_kernel"] if wl.a_dtype != "bf16" else []
+        return (["group_kernel", "grouped_stage1_kernel"], hot + [s2, "combine_kernel"])
     if wl.tokens * wl.topk <= 32:
         return (["stage1_kernel"], ["stage2_small_kernel"])
     return (["stage1_kernel"], ["stage2_kernel", "combine_kernel"])
@@ -310,9 +314,9 @@ def roofline(wl, r, traffic_key=None):
     recs = [counter_record(f"{k}:{wl.name}") for k in ks]
     tr = [None if x is None else x.get("hbm_bytes_per_launch") for x in recs]
     roof["traffic"] = None if any(t is None for t in tr) else int(sum(tr))
-    main = recs[-1] if ks[0] == "group_kernel" or len(ks) == 1 else recs[0]
-    if main is not None and main.get("mfma_util") is not None:
-        roof["mfma_busy_counter"] = main["mfma_util"]
+    busy = {k: x["mfma_util"] for k, x in zip(ks, recs) if x is not None and x.get("mfma_util") is not None}
+    if busy:
+        roof["mfma_busy_counter"] = busy     # MFMA-busy share of SIMD cycles, per kernel of the call
     return roof
 
 
@@ -346,10 +350,10 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 COPY_PROBE_BYTES = 1 << 30      # elementwise float32 negation of 1 GiB: reads and writes 1 GiB
 # (workload, stage call) pairs launched by --counter-probe: the headline's dominant kernel and
 # those of the largest tiers
-PROBES = [("dec-1", 1), ("dec-1", 2), ("dec-4", 1), ("dec-4", 2), ("mid-1024", 1), ("mid-1024", 2),
-          ("pre-16384", 1), ("pre-16384", 2), ("pre-a16-8192", 1), ("pre-a16-8192", 2), ("ep-8192", 1),
-          ("ep-8192", 2)]
-KERNEL_KEYS = ("grouped_stage1_kernel", "grouped_stage2_kernel", "stage2_small_kernel", "stage2_kernel",
+PROBES = [(w, st) for w in ("dec-1", "dec-4", "dec-16", "mid-256", "mid-1024", "pre-16384", "pre-a8-8192",
+                            "pre-a16-8192", "ep-8192") for st in (1, 2)]
+KERNEL_KEYS = ("grouped_stage1_kernel", "grouped_stage2_res_kernel", "grouped_stage2_kernel", "hot_stage2_kernel",
+               "hot_table_kernel", "stage2_small_kernel", "stage2_kernel",
                "stage1_kernel", "combine_kernel", "group_kernel")
 
 
