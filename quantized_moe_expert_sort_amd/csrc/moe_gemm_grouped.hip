@@ -550,7 +550,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
             aop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
           }
           const uint32_t sw = AW ? *reinterpret_cast<const uint32_t*>(slot + ar * 16 + kq) : AS1 ? las[ar] : 0u;
-          asc = (sw >> (8 * g)) & 0xFFu;
+          asc = sw;                                     // the byte is taken where it is used
         };
         constexpr int AD = F::AD;
         v8i aq[AD + 1];
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         for (int f = 0; f < NA; ++f) {
           if (f + AD < NA) load_a(f + AD, aq[(f + AD) % (AD + 1)], asq[(f + AD) % (AD + 1)]);
           const v8i& a_cur = aq[f % (AD + 1)];
-          const uint32_t as_cur = asq[f % (AD + 1)];
+          const uint32_t as_cur = (asq[f % (AD + 1)] >> (8 * g)) & 0xFFu;
 #pragma unroll
           for (int j = 0; j < NFW; ++j) {
             if (ADT == DT_FP8) acc[f][j] = mfma_fp8_fp4(a_cur, bop[j], acc[f][j], as_cur, bsc[j]);
@@ -898,7 +898,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
           } else {
             xop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
           }
-          xsc = (las[ar] >> (8 * g)) & 0xFFu;
+          xsc = las[ar];                                // the byte is taken where it is used
         };
         v8i x_cur;
         uint32_t xs_cur;
@@ -908,8 +908,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
           v8i x_nxt = x_cur;
           uint32_t xs_nxt = xs_cur;
           if (f + 1 < NA) load_x(f + 1, x_nxt, xs_nxt);
+          const uint32_t xb = (xs_cur >> (8 * g)) & 0xFFu;
 #pragma unroll
-          for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xs_cur);
+          for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xb);
           __builtin_amdgcn_sched_barrier(0);
           x_cur = x_nxt;
           xs_cur = xs_nxt;
@@ -1164,7 +1165,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedAr
           } else {
             xop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
           }
-          xsc = (las[ar] >> (8 * g)) & 0xFFu;
+          xsc = las[ar];                                // the byte is taken where it is used
         };
         v8i x_cur;
         uint32_t xs_cur;
@@ -1174,8 +1175,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedAr
           v8i x_nxt = x_cur;
           uint32_t xs_nxt = xs_cur;
           if (f + 1 < NA) load_x(f + 1, x_nxt, xs_nxt);
+          const uint32_t xb = (xs_cur >> (8 * g)) & 0xFFu;
 #pragma unroll
-          for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xs_cur);
+          for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xb);
           __builtin_amdgcn_sched_barrier(0);
           x_cur = x_nxt;
           xs_cur = xs_nxt;
@@ -1461,7 +1463,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
         } else {
           xop = fp4_operand_lo(*reinterpret_cast<const uint4*>(la + swz_slot<4>(ar, g) * 16));
         }
-        xsc = (las[ar] >> (8 * g)) & 0xFFu;
+        xsc = las[ar];                                  // the byte is taken where it is used
       };
       v8i x_cur;
       uint32_t xs_cur;
@@ -1471,8 +1473,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
         v8i x_nxt = x_cur;
         uint32_t xs_nxt = xs_cur;
         if (f + 1 < MF) load_x(f + 1, x_nxt, xs_nxt);
+        const uint32_t xb = (xs_cur >> (8 * g)) & 0xFFu;
 #pragma unroll
-        for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xs_cur);
+        for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(wop[j], x_cur, acc[f][j], wsc[j], xb);
         __builtin_amdgcn_sched_barrier(0);
         x_cur = x_nxt;
         xs_cur = xs_nxt;
