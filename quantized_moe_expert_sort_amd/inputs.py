@@ -134,10 +134,20 @@ def _element_lut(scale_byte):
     return lut
 
 
+def _top_code6_prob(scale_byte):
+    """P(magnitude code 6 | the block's largest value in the top binade [4, 8) x 2^sexp): the
+    share of [4, 8) that rounds to 4.0 rather than 6.0, under N(0, (0.02 / 2^sexp)^2)."""
+    sigma = _SIGMA_W / 2.0 ** (scale_byte - 127)
+    p6 = _phi_abs(5.0, sigma) - _phi_abs(4.0, sigma)
+    p7 = _phi_abs(8.0, sigma) - _phi_abs(5.0, sigma)
+    return p6 / (p6 + p7)
+
+
 _SCALES = _scale_byte_table()
 _SCALE_BYTES = np.array([s for s, _ in _SCALES], dtype=np.uint8)
 _SCALE_CDF = np.cumsum([p for _, p in _SCALES])
 _ELEM_LUTS = np.stack([_element_lut(int(s)) for s in _SCALE_BYTES])   # [nscale, 256]
+_TOP6 = np.array([_top_code6_prob(int(s)) for s in _SCALE_BYTES])
 
 
 def make_mxfp4_expert(seed, tensor_id, e, N, K):
@@ -152,6 +162,16 @@ def make_mxfp4_expert(seed, tensor_id, e, N, K):
         if j != main:
             sel = sidx == j
             codes[sel] = _ELEM_LUTS[j][u[sel]]
+    # A block's scale byte stands for the binade of its largest |value|, so (as in any block
+    # the 1x32 encoding produces) its largest magnitude code is 6 (4.0) or 7 (6.0): where the
+    # independent draws left every code below 6, one element, chosen at random, keeps its sign
+    # and takes magnitude 6 or 7.
+    low = (codes & 7).max(axis=-1) < 6
+    pick = rng.integers(0, 32, size=(N, K // 32))
+    top = np.where(rng.random((N, K // 32)) < _TOP6[sidx], 6, 7).astype(np.uint8)
+    r, c = np.nonzero(low)
+    el = pick[r, c]
+    codes[r, c, el] = (codes[r, c, el] & 8) | top[r, c]
     codes = codes.reshape(N, K)
     packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
     return packed.astype(np.uint8), _SCALE_BYTES[sidx]
