@@ -164,6 +164,16 @@ __device__ __forceinline__ uint32_t encode_pair_fp8_hw(float a, float b, int sex
   return (uint32_t)(uint16_t)r[0];
 }
 
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one lane of each 16-lane row), with the
+// gfx950 row swaps: permlane32_swap of a value with itself leaves lanes l and l ^ 32 holding
+// the two halves' values in its two results, permlane16_swap does the same for rows l and l ^ 16.
+__device__ __forceinline__ uint32_t cross_row_max_u32(uint32_t v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = h[0] > h[1] ? h[0] : h[1];
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return r[0] > r[1] ? r[0] : r[1];
+}
+
 // Reduce |v| bit patterns over the 32 lanes of a half-wave (xor shuffles stay inside it).
 __device__ __forceinline__ uint32_t halfwave_max_u32(uint32_t v) {
 #pragma unroll

@@ -292,6 +292,15 @@ __device__ __forceinline__ int swz_slot(int row, int part) {
 
 constexpr int NLOAD = 4;                      // loader waves
 
+// The grouped GEMMs take the fp4 weight rows as the MFMA's first operand and the activation /
+// intermediate rows as its second: lane (r, g) of a 16 x 16 accumulator then holds the four
+// consecutive weight rows (output columns) 4 g .. 4 g + 3 of activation row r.
+template <int ADT>
+__device__ __forceinline__ v4f mfma_w_x(const v8i& w, const v8i& x, const v4f& c, uint32_t sw, uint32_t sx) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, c, MFMA_FMT_FP4,
+                                                          ADT == DT_FP8 ? MFMA_FMT_FP8 : MFMA_FMT_FP4, 0, sw, 0, sx);
+}
+
 // bf16 activations / intermediate rows: an item takes one part of a group (up to 4 tiles, 128
 // rows), so the 256-byte A row pieces of a K step leave room for three buffers; the B side
 // (fp4 rows and their scales) is that of fp8 / fp4.
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-            for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_bf16(a_cur[jj], bop[j][jj], acc[f][j]);
+            for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_bf16(bop[j][jj], a_cur[jj], acc[f][j]);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -564,10 +573,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
           const v8i& a_cur = aq[f % (AD + 1)];
           const uint32_t as_cur = (asq[f % (AD + 1)] >> (8 * g)) & 0xFFu;
 #pragma unroll
-          for (int j = 0; j < NFW; ++j) {
-            if (ADT == DT_FP8) acc[f][j] = mfma_fp8_fp4(a_cur, bop[j], acc[f][j], as_cur, bsc[j]);
-            else acc[f][j] = mfma_fp4_fp4(a_cur, bop[j], acc[f][j], as_cur, bsc[j]);
-          }
+          for (int j = 0; j < NFW; ++j) acc[f][j] = mfma_w_x<ADT>(bop[j], a_cur, acc[f][j], bsc[j], as_cur);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -600,52 +606,54 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         uint8_t* st_codes = lds;                          // [BM][OBS]
         uint8_t* st_scales = lds + BM * F::OBS;           // [BM][4]: one byte per 32-column block
         const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
+        // lane (r16, g) holds, for row arow0 + 16 f + r16, the gate sums (fragments 0, 1) and
+        // the up sums (fragments 2, 3) of the four consecutive columns 32 wn + 16 h + 4 g + i:
+        // one 1x32 block per row and wave, its 32 values in the four lanes r16 + 16 g
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
+          const int row = arow0 + 16 * f + r16;
+          float y[2][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = arow0 + 16 * f + 4 * g + i;
-            // one 32-column block: gate fragments 0, 1 with up fragments 2, 3
-            float y[2];
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int i = 0; i < 4; ++i) {
               const float gs = acc[f][h][i], us = acc[f][2 + h][i];
-              y[h] = ACT == ACT_SITUV2 ? situv2(gs, us, p.beta, inv_beta, p.linear_beta, inv_lb) : silu_mul(gs, us);
+              y[h][i] = ACT == ACT_SITUV2 ? situv2(gs, us, p.beta, inv_beta, p.linear_beta, inv_lb) : silu_mul(gs, us);
             }
-            if constexpr (ADT == DT_BF16) {   // bf16 intermediate: an even lane stores its column and the next
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const uint32_t hb = f32_to_bf16_rne(y[h]);
-                const uint32_t hn = lane_xor1(hb);
-                const int c = 32 * wn + 16 * h + r16;
-                if ((r16 & 1) == 0) *reinterpret_cast<uint32_t*>(st_codes + row * F::OBS + 2 * c) = hb | (hn << 16);
-              }
-              continue;
-            }
-            const uint32_t amax =
-                row16_max_u32(max(__float_as_uint(y[0]) & 0x7FFFFFFFu, __float_as_uint(y[1]) & 0x7FFFFFFFu));
-            // the 1x32 rule with the hardware converts: an even lane encodes its column and the
-            // next one (the odd lane's value comes over DPP); an Inf / NaN block gets scale 255
-            // and zero codes
-            const bool bad = amax >= 0x7F800000u;
-            const int sexp = block_sexp_any(bad ? 0u : amax, ADT == DT_FP8 ? Fp8Fmt::EMAX : Fp4Fmt::EMAX);
-            const float scale = e8m0_scale_float(sexp);
+          if constexpr (ADT == DT_BF16) {   // bf16 intermediate: four columns in one 8-byte write
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const float yn = __uint_as_float(lane_xor1(__float_as_uint(y[h])));
-              const int c = 32 * wn + 16 * h + r16;
-              if ((r16 & 1) == 0) {
-                if (ADT == DT_FP8) {
-                  const uint32_t pr = bad ? 0u : encode_pair_fp8_hw(y[h], yn, sexp);
-                  *reinterpret_cast<uint16_t*>(st_codes + row * F::OBS + c) = (uint16_t)pr;
-                } else {
-                  const uint32_t pr = bad ? 0u : encode_pair_fp4_hw(y[h], yn, scale);
-                  st_codes[row * F::OBS + c / 2] = (uint8_t)pr;
-                }
-              }
+              const uint2 v = {(uint32_t)f32_to_bf16_rne(y[h][0]) | ((uint32_t)f32_to_bf16_rne(y[h][1]) << 16),
+                               (uint32_t)f32_to_bf16_rne(y[h][2]) | ((uint32_t)f32_to_bf16_rne(y[h][3]) << 16)};
+              *reinterpret_cast<uint2*>(st_codes + row * F::OBS + 2 * (32 * wn + 16 * h + 4 * g)) = v;
             }
-            st_scales[row * 4 + wn] = (uint8_t)(bad ? 255u : (uint32_t)(sexp + 127));
+            continue;
           }
+          uint32_t m = 0;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(y[h][i]) & 0x7FFFFFFFu);
+          const uint32_t amax = cross_row_max_u32(m);
+          // the 1x32 rule with the hardware converts, two columns per convert; an Inf / NaN
+          // block gets scale 255 and zero codes
+          const bool bad = amax >= 0x7F800000u;
+          const int sexp = block_sexp_any(bad ? 0u : amax, ADT == DT_FP8 ? Fp8Fmt::EMAX : Fp4Fmt::EMAX);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = 32 * wn + 16 * h + 4 * g;
+            if (ADT == DT_FP8) {
+              const uint32_t lo = bad ? 0u : encode_pair_fp8_hw(y[h][0], y[h][1], sexp);
+              const uint32_t hi = bad ? 0u : encode_pair_fp8_hw(y[h][2], y[h][3], sexp);
+              *reinterpret_cast<uint32_t*>(st_codes + row * F::OBS + c) = lo | (hi << 16);
+            } else {
+              const float scale = e8m0_scale_float(sexp);
+              const uint32_t lo = bad ? 0u : encode_pair_fp4_hw(y[h][0], y[h][1], scale);
+              const uint32_t hi = bad ? 0u : encode_pair_fp4_hw(y[h][2], y[h][3], scale);
+              *reinterpret_cast<uint16_t*>(st_codes + row * F::OBS + c / 2) = (uint16_t)(lo | (hi << 8));
+            }
+          }
+          st_scales[row * 4 + wn] = (uint8_t)(bad ? 255u : (uint32_t)(sexp + 127));
         }
         lds_barrier();
         if (!loader) {
@@ -701,12 +709,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 // next item's first P-1 steps before storing, and one item's output drains while the next
 // item's operands arrive (the loaders' waits count the stores issued after those copies).  The
 // rows are stored without the router weight; the combine applies it.
-
-template <int ADT>
-__device__ __forceinline__ v4f mfma_w_x(const v8i& w, const v8i& x, const v4f& c, uint32_t sw, uint32_t sx) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, c, MFMA_FMT_FP4,
-                                                          ADT == DT_FP8 ? MFMA_FMT_FP8 : MFMA_FMT_FP4, 0, sw, 0, sx);
-}
 
 // scalar (constant-cache) load of a wave-uniform address: counted by lgkmcnt, not vmcnt
 __device__ __forceinline__ int ld_const(const int32_t* p) {
