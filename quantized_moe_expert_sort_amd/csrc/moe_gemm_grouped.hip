@@ -292,6 +292,11 @@ __device__ __forceinline__ int swz_slot(int row, int part) {
 
 constexpr int NLOAD = 4;                      // loader waves
 
+// scalar (constant-cache) load of a wave-uniform address: counted by lgkmcnt, not vmcnt
+__device__ __forceinline__ int ld_const(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+
 // The grouped GEMMs take the fp4 weight rows as the MFMA's first operand and the activation /
 // intermediate rows as its second: lane (r, g) of a 16 x 16 accumulator then holds the four
 // consecutive weight rows (output columns) 4 g .. 4 g + 3 of activation row r.
@@ -351,11 +356,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
   constexpr bool AW = L1::AW, AS1 = L1::AS1, HAS_AS = AW || AS1;
   static_assert(F::A_IPL * NLOAD * 1024 == F::A_BYTES && F::B_IPL * NLOAD * 1024 == F::B_BYTES, "copy split");
   static_assert(BM <= NLOAD * WAVE && BNW == NLOAD * WAVE, "at most one scale copy of each operand per loader");
-  static_assert(BM * (F::OBS + 4) <= P * L1::BUF, "staging fits");
+  static_assert(BM * (F::OBS + 4) <= L1::BUF, "the staging tile fits one operand buffer");
   static_assert(P <= 5, "a chunk slot is refilled only after the four steps of its previous chunk");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L1::BYTES];
-  __shared__ int lds_v[BM];
+  __shared__ int lds_v[2][BM];                             // row ids of this item and the next
 
   const int TK = p.T * p.topk, D = p.D, I = p.I;
   const int lane = threadIdx.x & (WAVE - 1);
@@ -374,96 +379,143 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
   // consecutive items, so they run at the same time on CUs of one XCD and fetch the group's
   // activation rows into its L2 once; second parts (empty for most small groups) come last.
   constexpr int PARTS = GT / F::GTA;
-  const int ng = *num_groups;
+  const int ng = ld_const(num_groups);
   const int xcd = blockIdx.x & 7, stride = gridDim.x >> 3, local0 = blockIdx.x >> 3;
   const int per_part = (ng > xcd ? (ng - xcd + 7) / 8 : 0) * n_nblk;
   const int items_here = PARTS * per_part;
+  const size_t a_rowbytes = (size_t)K * KA / 128;
 
-  for (int local = local0; local < items_here; local += stride) {
+  // item `local`: its column block and the first tile and tile count of its rows (bf16: a group
+  // of up to GTA tiles is one part, a larger one two parts of ceil(n/2) and floor(n/2) tiles)
+  auto item_tiles = [&](int local, int& tile0, int& ntile, int& nb) {
     const int part = local >= per_part ? 1 : 0, rem = local - part * per_part;
-    const int gl = rem / n_nblk, nb = rem - gl * n_nblk;
-    const int gi = gl * 8 + xcd;
-    const int2 grp = groups[gi];
-    int tile0 = grp.x, ntile = grp.y;
-    if (PARTS == 2) {   // up to GTA tiles: one part; more: parts of ceil(n/2) and floor(n/2) tiles
-      const int h0 = grp.y <= F::GTA ? grp.y : (grp.y + 1) >> 1;
+    const int gl = rem / n_nblk;
+    nb = rem - gl * n_nblk;
+    const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
+    tile0 = ld_const(gp);
+    ntile = ld_const(gp + 1);
+    if (PARTS == 2) {
+      const int h0 = ntile <= F::GTA ? ntile : (ntile + 1) >> 1;
       tile0 += part ? h0 : 0;
-      ntile = part ? grp.y - h0 : h0;
+      ntile = part ? ntile - h0 : h0;
     }
-    if (ntile == 0) continue;                             // the empty second part of a small group
-    const int rows_used = ntile * 32;
-    const int e = p.expert_ids[tile0];
-    const int row_base = tile0 * 32;                      // first layout row of the group
-    if (threadIdx.x < BM) {                               // loader lanes
-      const int r = threadIdx.x;
-      lds_v[r] = r < rows_used ? p.sorted_ids[row_base + r] : TK;
+  };
+  // this workgroup's first item at or after `local` that has rows (only a bf16 second part can
+  // be empty), or items_here
+  auto next_item = [&](int local) {
+    if constexpr (PARTS == 2) {
+      for (; local < items_here; local += stride) {
+        int t0, nt, cb;
+        item_tiles(local, t0, nt, cb);
+        if (nt > 0) break;
+      }
     }
-    lds_barrier();
+    return local < items_here ? local : items_here;
+  };
 
-    // ---- copy sources.  A: the gathered x rows (padding rows read token 0, their results are
-    // never stored).  B: [gate NI | up NI] rows of column block nb (NI = BNW/2).
-    const size_t a_rowbytes = (size_t)K * KA / 128;
-    const uint8_t* a_base = p.x;
-    const uint8_t* as_base = p.xs;
-    const uint8_t* b_base = p.w1 + (size_t)e * 2 * I * (D / 2);
-    const uint8_t* bs_base = p.w1s + (size_t)e * 2 * I * (D / 32);
+  // Copy sources of an item.  A: the gathered x rows (padding rows read token 0, their results
+  // are never stored).  B: [gate NI | up NI] rows of column block nb (NI = BNW/2), one 1 KB block
+  // of packed w1 per 16 rows and step.  Loader lw issues tile instructions j = i * NLOAD + lw
+  // (A rows [j * ROWS_PER_AI, ...), instructions wholly past the group's rows are not issued;
+  // B rows [16 j, 16 j + 16)) and the scales of A rows and B rows [64 lw, 64 lw + 64).
+  struct Src {
+    const uint8_t *b, *bs;
+    uint32_t a_off[F::A_IPL], b_off[F::B_IPL], as_off, bs_off;
+    int n_ai, n_data, n_chunk, rows_used, row_base, nb;
+    bool as_on;
+  };
+  // every wave: the item's rows and column block; the loaders also the copy offsets (their
+  // rows' token ids read from the sorted layout) and the item's row ids in lds_v[vb]
+  auto make = [&](int local, Src& q, int vb) {
+    int tile0, ntile;
+    item_tiles(local, tile0, ntile, q.nb);
+    q.rows_used = ntile * 32;
+    q.row_base = tile0 * 32;
+    if (!loader) return;
+    const int e = ld_const(p.expert_ids + tile0);
+    q.b = p.w1 + (size_t)e * 2 * I * (D / 2);
+    q.bs = p.w1s + (size_t)e * 2 * I * (D / 32);
     auto b_row = [&](int r) -> int {                      // weight row within the expert
       constexpr int NI = BNW / 2;
-      return r < NI ? nb * NI + r : I + nb * NI + (r - NI);
+      return r < NI ? q.nb * NI + r : I + q.nb * NI + (r - NI);
     };
-    auto a_src_index = [&](int row) -> uint32_t {        // token row of A row `row`
-      const int v = lds_v[row];
-      return (uint32_t)((unsigned)v < (unsigned)TK ? v / p.topk : 0);
+    // the row ids of the loader's A rows and of its scale row (= its lds_v row), loaded together
+    // (indices clamped into the group; rows past it are padding); the lane index is re-derived
+    // here so that nothing computed from it stays live across the item loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int sc_row = lw * WAVE + ln;
+    int rid[F::A_IPL + 1];
+#pragma unroll
+    for (int i = 0; i < F::A_IPL; ++i)
+      rid[i] = p.sorted_ids[q.row_base + min(((i * NLOAD + lw) * WAVE + ln) / ACPR, q.rows_used - 1)];
+    rid[F::A_IPL] = p.sorted_ids[q.row_base + min(sc_row, q.rows_used - 1)];
+    auto tok = [&](int row, int v) -> uint32_t {          // token row of A row `row`
+      return (uint32_t)(row < q.rows_used && (unsigned)v < (unsigned)TK ? v / p.topk : 0);
     };
-    // loader lw issues tile instructions j = i * NLOAD + lw (A rows [j * ROWS_PER_AI, ...));
-    // A instructions wholly past the group's rows are not issued
-    uint32_t a_off[F::A_IPL];
     int n_ai = 0;
 #pragma unroll
     for (int i = 0; i < F::A_IPL; ++i) {
       const int j = i * NLOAD + lw;
-      const int q = j * WAVE + lane;
-      const int row = q / ACPR, part = swz_slot<ACPR>(row, q % ACPR) - row * ACPR;   // the XOR is an involution
-      a_off[i] = a_src_index(row) * (uint32_t)a_rowbytes + part * 16;
-      n_ai += j * F::ROWS_PER_AI < rows_used;
+      const int qq = j * WAVE + ln;
+      const int row = qq / ACPR, part = swz_slot<ACPR>(row, qq % ACPR) - row * ACPR;   // the XOR is an involution
+      q.a_off[i] = tok(row, rid[i]) * (uint32_t)a_rowbytes + part * 16;
+      n_ai += j * F::ROWS_PER_AI < q.rows_used;
     }
-    // B instruction j copies tile rows [16 j, 16 j + 16): weight rows b_row(16 j) .. + 15, one
-    // 1 KB block of packed w1 per step, to LDS bytes [1024 j, 1024 j + 1024) in the same order
-    uint32_t b_off[F::B_IPL];
 #pragma unroll
     for (int i = 0; i < F::B_IPL; ++i) {
       const int j = i * NLOAD + lw;
-      b_off[i] = (uint32_t)(b_row(16 * j) / 16) * (uint32_t)(S * 1024) + 16 * lane;
+      q.b_off[i] = (uint32_t)(b_row(16 * j) / 16) * (uint32_t)(S * 1024) + 16 * ln;
     }
-    // scales: loader lw copies those of A rows and of B rows [64 lw, 64 lw + 64)
-    const int sc_row = lw * WAVE + lane;
-    const bool as_on = HAS_AS && lw * WAVE < rows_used;   // rows_used <= BM
-    const uint32_t as_off = HAS_AS && sc_row < BM ? a_src_index(sc_row) * (uint32_t)(K / 32) : 0u;
-    const uint32_t bs_off = (uint32_t)b_row(sc_row) * (uint32_t)(K / 32);
+    q.as_on = HAS_AS && lw * WAVE < q.rows_used;          // rows_used <= BM
+    q.as_off = HAS_AS && sc_row < BM ? tok(sc_row, rid[F::A_IPL]) * (uint32_t)(K / 32) : 0u;
+    q.bs_off = (uint32_t)b_row(sc_row) * (uint32_t)(K / 32);
+    q.n_ai = n_ai;
     // copy instructions a loader issues for step s: the chunks travel with steps 0, 4, 8, ...
-    const int n_data = n_ai + F::B_IPL + (AS1 && as_on ? 1 : 0);
-    const int n_chunk = 1 + (AW && as_on ? 1 : 0);
+    q.n_data = n_ai + F::B_IPL + (AS1 && q.as_on ? 1 : 0);
+    q.n_chunk = 1 + (AW && q.as_on ? 1 : 0);
+    if (sc_row < BM) lds_v[vb][sc_row] = sc_row < q.rows_used ? rid[F::A_IPL] : TK;
+  };
+  // per step the K advance goes into the (scalar) global base; lane offsets stay fixed.  The
+  // chunk copies are issued first, so the wait for a step's tiles covers them.
+  auto issue = [&](const Src& q, int s, int buf) {
+    if ((s & 3) == 0) {
+      const uint32_t C = __builtin_amdgcn_readfirstlane(slot0 + ((s >> 2) & 1) * L1::SLOT);
+      const int cb = (s >> 2) * 16;
+      if (AW && q.as_on) dma16(p.xs + cb, q.as_off, C + lw * 1024);
+      dma16(q.bs + cb, q.bs_off, C + L1::A_SLOT + lw * 1024);
+    }
+    const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * L1::BUF);
+    const uint8_t* ab = p.x + s * KA;
+    const uint8_t* bb = q.b + s * 1024;
+#pragma unroll
+    for (int i = 0; i < F::A_IPL; ++i)
+      if (i < q.n_ai) dma16(ab, q.a_off[i], L + (i * NLOAD + lw) * 1024);
+#pragma unroll
+    for (int i = 0; i < F::B_IPL; ++i)
+      dma16(bb, q.b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
+    if (AS1 && q.as_on) dma4(p.xs + s * 4, q.as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
+  };
 
-    // per step the K advance goes into the (scalar) global base; lane offsets stay fixed.  The
-    // chunk copies are issued first, so the wait for a step's tiles covers them.
-    auto issue = [&](int s, int buf) {
-      if ((s & 3) == 0) {
-        const uint32_t C = __builtin_amdgcn_readfirstlane(slot0 + ((s >> 2) & 1) * L1::SLOT);
-        const int cb = (s >> 2) * 16;
-        if (AW && as_on) dma16(as_base + cb, as_off, C + lw * 1024);
-        dma16(bs_base + cb, bs_off, C + L1::A_SLOT + lw * 1024);
-      }
-      const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * L1::BUF);
-      const uint8_t* ab = a_base + s * KA;
-      const uint8_t* bb = b_base + s * 1024;
+  // The first P-1 steps of an item are issued before its K loop: for the first item here, for
+  // every later one during the epilogue of the item before (its staging tile sits in buffer
+  // P-1, the copies go to buffers 0 .. P-2), so an item's first operands are in flight while the
+  // previous item's activation, re-encode and stores run.
+  Src cur, nxt;
+  int local = next_item(local0), vb = 0;
+  if (local < items_here) {
+    make(local, cur, 0);
+    if (loader) {
 #pragma unroll
-      for (int i = 0; i < F::A_IPL; ++i)
-        if (i < n_ai) dma16(ab, a_off[i], L + (i * NLOAD + lw) * 1024);
-#pragma unroll
-      for (int i = 0; i < F::B_IPL; ++i)
-        dma16(bb, b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
-      if (AS1 && as_on) dma4(as_base + s * 4, as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
-    };
+      for (int q = 0; q < P - 1; ++q)
+        if (q < S) issue(cur, q, q);
+    }
+  }
+  lds_barrier();                                          // lds_v[0] is complete
+
+  while (local < items_here) {
+    const int nl = next_item(local + stride);
+    const int rows_used = cur.rows_used, row_base = cur.row_base, nb = cur.nb;
 
     // the wave's B fragment rows: gate rows [32wn, 32wn+32) and the same up rows
     auto b_frag_row = [&](int j) -> int { return j < 2 ? 32 * wn + 16 * j : BNW / 2 + 32 * wn + 16 * (j - 2); };
@@ -583,28 +635,31 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
       };
 
       // ---- K loop: steps s+1 .. s+P-2 in flight while step s is computed
-      if (loader) {
-#pragma unroll
-        for (int q = 0; q < P - 1; ++q)
-          if (q < S) issue(q, q);
-      }
       for (int s = 0; s < S; ++s) {
         // a loader's copies of step s are done once at most those of the later steps in
         // flight remain
         int later = 0;
 #pragma unroll
         for (int t = 1; t <= P - 2; ++t)
-          if (s + t < S) later += n_data + (((s + t) & 3) == 0 ? n_chunk : 0);
+          if (s + t < S) later += cur.n_data + (((s + t) & 3) == 0 ? cur.n_chunk : 0);
         wait_and_barrier(loader ? later : 63);
-        if (loader && s + P - 1 < S) issue(s + P - 1, (s + P - 1) % P);   // refills the buffer of step s-1
+        if (loader && s + P - 1 < S) issue(cur, s + P - 1, (s + P - 1) % P);   // refills the buffer of step s-1
         if (NA > 0) compute(s);
       }
-      lds_barrier();                                      // the operand buffers become staging
+      lds_barrier();                                      // every operand read of the item is done
+      if (nl < items_here) {                              // the next item's first steps
+        make(nl, nxt, vb ^ 1);
+        if (loader) {
+#pragma unroll
+          for (int q = 0; q < P - 1; ++q)
+            if (q < S) issue(nxt, q, q);
+        }
+      }
 
-      // ---- epilogue: the item's output tile is staged in LDS by every wave
+      // ---- epilogue: the item's output tile is staged in LDS buffer P-1 by every wave
       {
-        uint8_t* st_codes = lds;                          // [BM][OBS]
-        uint8_t* st_scales = lds + BM * F::OBS;           // [BM][4]: one byte per 32-column block
+        uint8_t* st_codes = lds + (P - 1) * L1::BUF;      // [BM][OBS]
+        uint8_t* st_scales = st_codes + BM * F::OBS;      // [BM][4]: one byte per 32-column block
         const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
         // lane (r16, g) holds, for row arow0 + 16 f + r16, the gate sums (fragments 0, 1) and
         // the up sums (fragments 2, 3) of the four consecutive columns 32 wn + 16 h + 4 g + i:
@@ -662,14 +717,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
           const size_t irow = ADT == DT_FP8 ? (size_t)I : ADT == DT_FP4 ? (size_t)I / 2 : (size_t)I * 2;   // intermediate row bytes
           for (int c = t; c < rows_used * CPRO; c += (GWAVES - NLOAD) * WAVE) {
             const int row = c / CPRO, part = c - row * CPRO;
-            if ((unsigned)lds_v[row] < (unsigned)TK) {
+            if ((unsigned)lds_v[vb][row] < (unsigned)TK) {
               const size_t R = (size_t)row_base + row;
               *reinterpret_cast<uint4*>(p.inter + R * irow + (size_t)nb * F::OB + part * 16) =
                   *reinterpret_cast<const uint4*>(st_codes + row * F::OBS + part * 16);
             }
           }
           for (int row = t; ADT != DT_BF16 && row < rows_used; row += (GWAVES - NLOAD) * WAVE) {
-            if ((unsigned)lds_v[row] < (unsigned)TK) {
+            if ((unsigned)lds_v[vb][row] < (unsigned)TK) {
               const size_t R = (size_t)row_base + row;
               *reinterpret_cast<uint32_t*>(p.inter_s + R * (I / 32) + (size_t)nb * 4) =
                   *reinterpret_cast<const uint32_t*>(st_scales + row * 4);
@@ -694,7 +749,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         default: run(std::integral_constant<int, 8>{}); break;
       }
     }
-    lds_barrier();                                        // lds_v and the staging tile are reused
+    lds_barrier();                                        // the staging tile and lds_v[vb] are reused
+    cur = nxt;
+    local = nl;
+    vb ^= 1;
   }
 }
 
@@ -709,11 +767,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 // next item's first P-1 steps before storing, and one item's output drains while the next
 // item's operands arrive (the loaders' waits count the stores issued after those copies).  The
 // rows are stored without the router weight; the combine applies it.
-
-// scalar (constant-cache) load of a wave-uniform address: counted by lgkmcnt, not vmcnt
-__device__ __forceinline__ int ld_const(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
-}
 
 template <int ADT>
 __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p, const int2* __restrict__ groups,
