@@ -165,7 +165,8 @@ static inline size_t moe_rowout_elem_bytes(int32_t a_dtype) { (void)a_dtype; ret
  *   inter     [cap*bm + 1, I] Stage1 intermediate in a_dtype (codes), in layout-row order; the
  *             extra last row is a zero row the token-major Stage2 reads for absent (token, expert)
  *             pairs;  iscale: its [cap*bm + 1, I/32] e8m0 scales (fp8 / fp4);
- *   groups    [cap] (first tile, tile count) groups of one expert's tiles, then their count;
+ *   groups    [cap] (first tile, tile count) groups of one expert's tiles, then their count and
+ *             eight work counters of the large-batch Stage1;
  *   cgroups   the same list without the token-major (hot) experts' groups, then its count;
  *   tile_hot  [cap] hot index of each tile's expert or -1;  hot_e: [MOE_HOT_MAX] hot experts and
  *             their count;

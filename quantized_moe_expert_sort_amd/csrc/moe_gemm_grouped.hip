@@ -220,6 +220,7 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_kernel(const int32_t* __r
       *num_cgroups = totc[0];
       hot_e[HOT_MAX_G] = nh;
     }
+    if (threadIdx.x < 8) num_groups[1 + threadIdx.x] = 0;   // the grouped Stage1's work counters
   };
   if (in_lds)
     work([&](int i) { return lds_e[i]; });
@@ -361,6 +362,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L1::BYTES];
   __shared__ int lds_v[2][BM];                             // row ids of this item and the next
+  __shared__ int s_claim;                                  // the item after the next one
 
   const int TK = p.T * p.topk, D = p.D, I = p.I;
   const int lane = threadIdx.x & (WAVE - 1);
@@ -497,12 +499,20 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
     if (AS1 && q.as_on) dma4(p.xs + s * 4, q.as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
   };
 
+  // Items are taken two ahead: the first two of a workgroup are local0 and local0 + stride; with
+  // fp8 / fp4 rows every later one is claimed from the XCD's work counter (zeroed by the group
+  // kernel) during the epilogue of the item before the next, so workgroups that drew smaller
+  // groups take more items; bf16 items (whose second parts may be empty) keep the fixed stride.
+  constexpr bool DYN = PARTS == 1;
+  int32_t* const ctr = const_cast<int32_t*>(num_groups) + 1 + xcd;
+
   // The first P-1 steps of an item are issued before its K loop: for the first item here, for
   // every later one during the epilogue of the item before (its staging tile sits in buffer
   // P-1, the copies go to buffers 0 .. P-2), so an item's first operands are in flight while the
   // previous item's activation, re-encode and stores run.
   Src cur, nxt;
   int local = next_item(local0), vb = 0;
+  int nl = local < items_here ? next_item(local + stride) : items_here;
   if (local < items_here) {
     make(local, cur, 0);
     if (loader) {
@@ -514,7 +524,6 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
   lds_barrier();                                          // lds_v[0] is complete
 
   while (local < items_here) {
-    const int nl = next_item(local + stride);
     const int rows_used = cur.rows_used, row_base = cur.row_base, nb = cur.nb;
 
     // the wave's B fragment rows: gate rows [32wn, 32wn+32) and the same up rows
@@ -658,6 +667,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 
       // ---- epilogue: the item's output tile is staged in LDS buffer P-1 by every wave
       {
+        // the first storer wave claims the item after the next one (its result is read after
+        // the activation math; this wave waits on no copies)
+        int claim = 0;
+        if (DYN && wave == NLOAD && lane == 0 && nl < items_here) claim = atomicAdd(ctr, 1);
         uint8_t* st_codes = lds + (P - 1) * L1::BUF;      // [BM][OBS]
         uint8_t* st_scales = st_codes + BM * F::OBS;      // [BM][4]: one byte per 32-column block
         const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
@@ -710,6 +723,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
           }
           st_scales[row * 4 + wn] = (uint8_t)(bad ? 255u : (uint32_t)(sexp + 127));
         }
+        if (DYN && wave == NLOAD && lane == 0) s_claim = nl < items_here ? min(2 * stride + claim, items_here) : items_here;
         lds_barrier();
         if (!loader) {
           const int t = threadIdx.x - NLOAD * WAVE;
@@ -750,8 +764,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
       }
     }
     lds_barrier();                                        // the staging tile and lds_v[vb] are reused
+    const int nn = DYN ? __builtin_amdgcn_readfirstlane(s_claim) : (nl < items_here ? next_item(nl + stride) : items_here);
     cur = nxt;
     local = nl;
+    nl = nn;
     vb ^= 1;
   }
 }
