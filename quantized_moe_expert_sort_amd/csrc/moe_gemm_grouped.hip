@@ -270,15 +270,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Position of 16-byte chunk `part` of row `row` in a row-major LDS tile with CPR chunks per row.
-// A matrix-core operand read has the 16 lanes of a group read chunk `part` of 16 consecutive
-// rows; the XOR makes those 16 chunks fall in distinct banks whether the LDS serves 16 lanes
-// over 64 four-byte banks or 8 lanes over 32 banks per cycle.  The XOR term depends only on
-// row % 16, so the fragments of a wave differ by constant offsets.
+// A matrix-core operand read has the 16 lanes of a group read chunk `part` of 16 rows (16
+// consecutive rows, or for the interleaved Stage2 weight rows rows {0-3, 8-11, 16-19, 24-27} of
+// a 32-row block, plus 4); the XOR term (a function of the row only, so the fragments of a
+// wave differ by constant offsets) spreads those reads over the banks.  For 64-byte rows it
+// flips chunk bit 1 in rows with bit 3 set: on gfx950 a 16-byte read of chunk c from rows r and
+// r + 8 costs a second LDS cycle (bank-conflict counter, microbenchmark over every XOR key of
+// row bits 0-4: this key reads all three row sets conflict-free; the 128-byte key reads 16
+// consecutive rows conflict-free).
 template <int CPR>
 __device__ __forceinline__ int swz_slot(int row, int part) {
   if constexpr (CPR == 16) return row * 16 + (part ^ (row & 15));
   else if constexpr (CPR == 8) return row * 8 + (part ^ (((row >> 1) ^ (row << 2)) & 7));
-  else return row * 4 + (part ^ ((row ^ (row >> 2)) & 3));
+  else return row * 4 + (part ^ ((row >> 2) & 2));
 }
 
 // ---------------------------------------------------------------- grouped GEMM
