@@ -101,6 +101,11 @@ SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
     (2500, 40, 6, 1024, 128, 0, 40, 32, "bf16", "silu", 0.0),
     (3000, 64, 8, 1024, 384, 16, 24, 32, "bf16", "situv2", 0.0),
     (2048, 64, 5, 512, 256, 0, 64, 32, "bf16", "situv2", 0.0),    # ~5-tile groups: parts of 3 + 2 tiles
+    # ~1000 skewed items: several per workgroup, so the next-item prefetch and (fp8 / fp4) the
+    # per-XCD work claims run, next to hot experts and the resident-row Stage2
+    (4096, 512, 8, 512, 256, 0, 512, 32, "fp8", "situv2", 0.7),
+    (4096, 512, 8, 512, 256, 0, 512, 32, "fp4", "silu", 0.7),
+    (4096, 512, 8, 512, 256, 0, 512, 32, "bf16", "situv2", 0.7),
     # experts with at least a quarter of the tokens' rows: token-major Stage2 for up to 16 of them
     (2048, 24, 16, 512, 256, 0, 24, 32, "fp4", "silu", 0.3),      # all 24 qualify: 16 token-major
     (2100, 24, 16, 512, 256, 0, 24, 32, "fp8", "situv2", 0.0),    # partial last 128-token tile
