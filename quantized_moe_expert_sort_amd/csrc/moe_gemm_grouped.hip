@@ -532,13 +532,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
 
     // the wave's B fragment rows: gate rows [32wn, 32wn+32) and the same up rows
     auto b_frag_row = [&](int j) -> int { return j < 2 ? 32 * wn + 16 * j : BNW / 2 + 32 * wn + 16 * (j - 2); };
-    const int arow0 = (BM / WM) * wm;                     // the wave's first A row
-    // A fragments of this wave that hold group rows: rows_used is a multiple of 32, so 0, 2, 4,
-    // 6 or 8 (bf16: 0, 2 or 4); the MFMA loop is instantiated per count (no per-fragment
-    // branches inside it).  (Alternating the fragments between the two wave rows, which evens
-    // out the waves of a SIMD for any group size, measured 13-18% slower here at fp8 / fp4; it
-    // also doubles the instantiations of this loop.)
-    const int n_af = max(0, min(MF, (rows_used - arow0) / 16));
+    // A fragments of a wave: with fp8 / fp4 rows they alternate between the two wave rows
+    // (fragment f of wave row wm holds rows 16 (2 f + wm) .. + 15), so the two waves of a SIMD
+    // (w and w + 4) get the same count, rows_used / 32, for any group size (ep-8192 Stage1
+    // 501 -> 481 us, pre-a8-8192 504 -> 485); bf16 keeps contiguous row halves (measured 1%
+    // faster there), 0, 2 or 4 fragments.  The MFMA loop is instantiated per count (no
+    // per-fragment branches inside it).
+    constexpr bool ALT = ADT != DT_BF16;
+    constexpr int FS = ALT ? 32 : 16;                      // row step between a wave's fragments
+    const int arow0 = ALT ? 16 * wm : (BM / WM) * wm;      // the wave's first A row
+    const int n_af = max(0, min(MF, ALT ? (rows_used - arow0 + 31) / 32 : (rows_used - arow0) / 16));
 
     auto run = [&](auto na_c) {
       constexpr int NA = decltype(na_c)::value;
@@ -570,7 +573,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
           bop[j][3] = fp4x8_to_bf16(q.w, sc);
         }
         auto load_a = [&](int f, v8bf* a) {
-          const int ar = arow0 + 16 * f + r16;
+          const int ar = arow0 + FS * f + r16;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const uint4 q = *reinterpret_cast<const uint4*>(la + swz_slot<16>(ar, 4 * g + jj) * 16);
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         // takes longer than the four MFMAs of one fragment); the scheduling barrier keeps the
         // compiler from hoisting every fragment read (register pressure)
         auto load_a = [&](int f, v8i& aop, uint32_t& asc) {
-          const int ar = arow0 + 16 * f + r16;
+          const int ar = arow0 + FS * f + r16;
           if (ADT == DT_FP8) {
             const uint4 lo = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, g) * 16);
             const uint4 hi = *reinterpret_cast<const uint4*>(la + swz_slot<8>(ar, 4 + g) * 16);
@@ -678,12 +681,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         uint8_t* st_codes = lds + (P - 1) * L1::BUF;      // [BM][OBS]
         uint8_t* st_scales = st_codes + BM * F::OBS;      // [BM][4]: one byte per 32-column block
         const float inv_beta = 1.0f / p.beta, inv_lb = 1.0f / p.linear_beta;
-        // lane (r16, g) holds, for row arow0 + 16 f + r16, the gate sums (fragments 0, 1) and
+        // lane (r16, g) holds, for row arow0 + FS f + r16, the gate sums (fragments 0, 1) and
         // the up sums (fragments 2, 3) of the four consecutive columns 32 wn + 16 h + 4 g + i:
         // one 1x32 block per row and wave, its 32 values in the four lanes r16 + 16 g
 #pragma unroll
         for (int f = 0; f < NA; ++f) {
-          const int row = arow0 + 16 * f + r16;
+          const int row = arow0 + FS * f + r16;
           float y[2][4];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
@@ -758,12 +761,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
         default: run(std::integral_constant<int, 4>{}); break;
       }
     } else {
-      static_assert(MF == 8, "fragment counts");
+      static_assert(MF == 8 && ALT, "fragment counts");
       switch (n_af) {
         case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
         case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
         case 4: run(std::integral_constant<int, 4>{}); break;
+        case 5: run(std::integral_constant<int, 5>{}); break;
         case 6: run(std::integral_constant<int, 6>{}); break;
+        case 7: run(std::integral_constant<int, 7>{}); break;
         default: run(std::integral_constant<int, 8>{}); break;
       }
     }
