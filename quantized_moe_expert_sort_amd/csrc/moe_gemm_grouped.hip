@@ -1355,9 +1355,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedAr
 
 constexpr int HOT_MAX = MOE_HOT_MAX;
 // Thread = token: its layout row and router weight for each hot expert (the zero row and 0 for a
-// hot expert it does not route to) and the mask of its slots whose expert is hot; workgroup 0
-// also clears the zero row of the intermediate.  Nothing is written when no expert is hot.
+// hot expert it does not route to; the sum of the weights when it routes to one twice) and the
+// mask of its slots whose expert is hot; workgroup 0 also clears the zero row of the
+// intermediate.  Nothing is written when no expert is hot.
 constexpr int TABLE_THREADS = 256;
+static_assert(HOT_MAX % 4 == 0, "the tables are written 16 bytes at a time");
 __global__ __launch_bounds__(TABLE_THREADS) void hot_table_kernel(FusedArgs p, int zrow, int row_bytes) {
   const int nh = p.hot_e[HOT_MAX];
   if (nh == 0) return;
@@ -1368,23 +1370,48 @@ __global__ __launch_bounds__(TABLE_THREADS) void hot_table_kernel(FusedArgs p, i
   }
   const int t = blockIdx.x * TABLE_THREADS + threadIdx.x;
   if (t >= p.T) return;
-  int32_t* pos = p.hotpos + (size_t)t * HOT_MAX;
-  float* wt = p.hotw + (size_t)t * HOT_MAX;
+  const int K = p.topk;
+  int pos[HOT_MAX];
+  float wt[HOT_MAX];
 #pragma unroll
   for (int h = 0; h < HOT_MAX; ++h) {
     pos[h] = zrow;
     wt[h] = 0.f;
   }
   uint32_t mask = 0;
-  for (int k = 0; k < p.topk; ++k) {
-    const int64_t v = (int64_t)t * p.topk + k;
-    const int r = p.row_of[v];
-    if (r < 0) continue;
-    const int h = p.tile_hot[r / 32];
-    if (h < 0) continue;
-    pos[h] = r;
-    wt[h] = p.topk_w[v];
-    mask |= 1u << k;
+  // a batch of slots: row positions and router weights loaded together (indices clamped into the
+  // token's slots), then their tiles' hot indices, then the slots taken in ascending k.  Two slots
+  // of one token on the same hot expert hold the same intermediate row: their weights add up.
+  constexpr int KB = 16;
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    int r[KB], hk[KB];
+    float w[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int64_t v = (int64_t)t * K + min(k0 + u, K - 1);
+      r[u] = p.row_of[v];
+      w[u] = p.topk_w[v];
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) hk[u] = p.tile_hot[max(r[u], 0) / 32];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const bool on = k0 + u < K && r[u] >= 0 && hk[u] >= 0;
+#pragma unroll
+      for (int h = 0; h < HOT_MAX; ++h) {
+        const bool m = on && hk[u] == h;
+        pos[h] = m ? r[u] : pos[h];
+        wt[h] += m ? w[u] : 0.f;
+      }
+      mask |= on ? 1u << (k0 + u) : 0u;
+    }
+  }
+  int4* pv = reinterpret_cast<int4*>(p.hotpos + (size_t)t * HOT_MAX);
+  float4* wv = reinterpret_cast<float4*>(p.hotw + (size_t)t * HOT_MAX);
+#pragma unroll
+  for (int q = 0; q < HOT_MAX / 4; ++q) {
+    pv[q] = int4{pos[4 * q], pos[4 * q + 1], pos[4 * q + 2], pos[4 * q + 3]};
+    wv[q] = float4{wt[4 * q], wt[4 * q + 1], wt[4 * q + 2], wt[4 * q + 3]};
   }
   p.hotmask[t] = mask;
 }

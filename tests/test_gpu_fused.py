@@ -132,6 +132,31 @@ def test_fused_small_full_output(T, Er, K, D, I, eb, E, bm, a_dtype, act, zipf):
     assert_rows_close(got, ref, local, TOL[a_dtype], f"{a_dtype} {act}", explain=ex)
 
 
+@pytest.mark.parametrize("T,a_dtype", [(2048, "fp4"), (2100, "fp8"), (2048, "bf16"), (300, "fp8")])
+def test_fused_repeated_expert_ids(T, a_dtype):
+    # a token that names one expert twice: two identical intermediate rows, both weighted into
+    # its sum (with fp8 / fp4 at 2048+ tokens every expert here is hot: the token-major Stage2
+    # adds the two router weights)
+    E, K, D, I = 24, 16, 512, 256
+    seed = 4242 + T
+    ids, w = gen.make_routing(seed, T, E, K, 0.3)
+    ids = ids.copy()
+    rep = np.arange(T) % 3 == 0
+    ids[rep, 1] = ids[rep, 0]
+    ids[np.arange(T) % 5 == 0, K - 1] = ids[np.arange(T) % 5 == 0, 2]
+    x = gen.make_x(seed, T, D)
+    w1, w1s, w2, w2s = gen.make_weights(seed, E, D, I)
+    wd = qm.device_weights(w1, w1s, w2, w2s)
+    print(f"repeated ids T={T} {a_dtype}", flush=True)
+    out, lay, ws = run_gpu(x, ids, w, wd, 0, E, 32, a_dtype, "situv2", keep_ws=True)
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref, inter = om.moe_fused(x, a_dtype, w1, w1s, w2, w2s, ids, w, 0, E, "situv2", BETA, LBETA,
+                              return_intermediate=True)
+    local = np.ones(T, bool)
+    ex = explainer(got, ws, lay, inter, None, a_dtype, "situv2", (w1, w1s, w2, w2s), ids, w, 0, D, I)
+    assert_rows_close(got, ref, local, TOL[a_dtype], f"repeated ids {a_dtype}", explain=ex)
+
+
 @pytest.mark.parametrize("a_dtype", ["bf16", "fp8", "fp4"])
 @pytest.mark.parametrize("bm", [16, 32])
 def test_stage1_exact_integer_sums(a_dtype, bm):
