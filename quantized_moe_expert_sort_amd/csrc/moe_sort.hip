@@ -44,7 +44,15 @@ __device__ __forceinline__ int bits_for(int n) {   // bits needed to write 0 .. 
   return b;
 }
 
-// Rank the rows [base, base + n_in) of one chunk.  On return (after a barrier):
+// Rows of one wave's sub-chunk: a chunk of n_in rows is split evenly over the waves in whole
+// rounds of 64 rows, so a short chunk still spreads over every wave (a 256-row chunk was
+// ranked by one wave when each wave took a fixed 512).
+__device__ __forceinline__ int sub_rows(int n_in) {
+  return min(SUB, (n_in + SORT_WAVES * WAVE - 1) / (SORT_WAVES * WAVE) * WAVE);
+}
+
+// Rank the rows [base, base + n_in) of one chunk (wave w takes rows [w*sub, w*sub + sub),
+// sub = sub_rows(n_in)).  On return (after a barrier):
 //   wc[w*E + e]  exclusive prefix over waves of the rows of expert e (per wave sub-chunk),
 //   tot[e]       rows of expert e in the chunk (if tot != nullptr),
 //   key[r]       local expert of this lane's row in round r (-1 if skipped),
@@ -54,11 +62,11 @@ __device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ ids, int6
                                            int key[ROUNDS], int rank[ROUNDS]) {
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
   for (int i = threadIdx.x; i < SORT_WAVES * E; i += SORT_THREADS) wc[i] = 0;
-  const int first = w * SUB;
+  const int sub = sub_rows(n_in), first = w * sub;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {                 // issue every load before using any
     const int idx = first + r * WAVE + lane;
-    key[r] = idx < n_in ? ids[base + idx] - expert_begin : -1;
+    key[r] = r * WAVE < sub && idx < n_in ? ids[base + idx] - expert_begin : -1;
   }
   __syncthreads();
   const int kb = bits_for(E);
@@ -70,7 +78,7 @@ __device__ __forceinline__ void rank_chunk(const int32_t* __restrict__ ids, int6
     k = (k >= 0 && k < E) ? k : -1;
     key[r] = k;
     rank[r] = 0;
-    if (first + r * WAVE >= n_in) continue;          // uniform: nothing left in this wave
+    if (r * WAVE >= sub || first + r * WAVE >= n_in) continue;   // uniform: nothing left in this wave
     const bool valid = k >= 0;
     const uint64_t same = match_any(k, valid, kb);
     if (valid) {
@@ -237,12 +245,12 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x == 0) *L.num_tiles = total;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  const int sentinel = n;
+  const int sentinel = n, sub = sub_rows(n);
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     if (r % (int)gridDim.x != (int)blockIdx.x) continue;
-    const int v = w * SUB + r * WAVE + lane;
-    if (v >= n) continue;
+    const int v = w * sub + r * WAVE + lane;
+    if (r * WAVE >= sub || v >= n) continue;
     const int k = key[r];
     if (k < 0) {
       if (L.row_of) L.row_of[v] = -1;
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r)
-    if (key[r] >= 0) ranks[base + w * SUB + r * WAVE + lane] = rank[r];
+    if (key[r] >= 0) ranks[base + w * sub_rows(n_in) + r * WAVE + lane] = rank[r];
   for (int e = threadIdx.x; e < E; e += SORT_THREADS) hist[(int64_t)blockIdx.x * E + e] = tot[e];
 }
 
