@@ -134,8 +134,10 @@ static inline int32_t moe_cap_tiles(int32_t tokens, int32_t topk, int32_t num_lo
 /* Most local experts moe_sort handles. */
 #define MOE_SORT_MAX_EXPERTS 2048
 
-/* Routed rows are counted in chunks of this many flat indices. */
+/* Routed rows are counted in chunks of MOE_SORT_MIN_CHUNK to MOE_SORT_CHUNK flat indices (the
+ * sort takes the size from the number of rows: about 64 chunks). */
 #define MOE_SORT_CHUNK 4096
+#define MOE_SORT_MIN_CHUNK 1024
 
 static inline size_t moe_align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -143,7 +145,7 @@ static inline size_t moe_align256(size_t b) { return (b + 255) & ~(size_t)255; }
  * and per-row ranks (int32). */
 static inline size_t moe_sort_ws_bytes(int32_t tokens, int32_t topk, int32_t num_local_experts) {
   int64_t n = (int64_t)tokens * topk;
-  int64_t chunks = (n + MOE_SORT_CHUNK - 1) / MOE_SORT_CHUNK;
+  int64_t chunks = (n + MOE_SORT_MIN_CHUNK - 1) / MOE_SORT_MIN_CHUNK;
   return moe_align256((size_t)(chunks + 2) * (size_t)num_local_experts * 4) + moe_align256((size_t)n * 4);
 }
 

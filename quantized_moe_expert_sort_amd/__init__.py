@@ -20,6 +20,7 @@ ACTS = {"situv2": ACT_SITUV2, "silu": ACT_SILU, "none_test": ACT_NONE_TEST}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_CAPACITY",
           4: "MOE_ERR_HIP", 5: "MOE_ERR_WORKSPACE"}
 SORT_CHUNK = 4096
+SORT_MIN_CHUNK = 1024
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 EXPORTS = ("moe_sort", "moe_quant_act", "moe_pack_w1", "moe_fused", "moe_fused_noalloc", "moe_last_hip_error")
@@ -115,7 +116,7 @@ def sync_words(tokens, cap):
 
 def sort_ws_bytes(tokens, topk, num_local_experts):
     n = tokens * topk
-    chunks = (n + SORT_CHUNK - 1) // SORT_CHUNK
+    chunks = (n + SORT_MIN_CHUNK - 1) // SORT_MIN_CHUNK
     return _align256((chunks + 2) * num_local_experts * 4) + _align256(n * 4)
 
 

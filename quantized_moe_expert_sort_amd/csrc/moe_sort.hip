@@ -2,16 +2,17 @@
 // (github ROCm/aiter PR 5118, "Summary": moe_sorting pads every expert up to a full block_m).
 //
 // The layout is unique (experts ascending, rows ascending in v = t*topk + k, sentinel T*topk on
-// padding), so the kernels rank rows without atomics.  A chunk of CHUNK rows is split into
+// padding), so the kernels rank rows without atomics.  A chunk of rows is split into
 // contiguous per-wave sub-chunks; inside a wave the rank of a row among the lanes holding the
 // same expert comes from per-bit ballots (a match-any), each wave keeps its own 16-bit counters
 // in LDS, and an exclusive scan over waves, chunks and experts (in index order) turns the
 // counts into positions.
 //
 //   rows <= 64    : one wave, ranks and offsets from ballots and cross-lane reads only.
-//   rows <= CHUNK : one workgroup does counting, scan, padding and scatter.
-//   larger        : count (one workgroup per chunk) -> scan (one workgroup)
-//                   -> scatter (one workgroup per chunk).
+//   rows <= 4096  : eight workgroups each rank every row and scan the experts, then write one
+//                   round of rows each.
+//   larger        : count (one workgroup per chunk of 1024 to 4096 rows) -> scan (one
+//                   workgroup) -> scatter (one workgroup per 1024 rows).
 // The layout's optional sync words are zeroed by the single-wave / single-workgroup kernel or,
 // on the multi-chunk path, by the counting kernel.
 #include "moe_kernels.h"
@@ -283,13 +284,13 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
 // ---------------------------------------------------------------- multi-chunk path
 
 __global__ __launch_bounds__(SORT_THREADS) void sort_count_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int expert_begin, int E, int* __restrict__ hist,
+    const int32_t* __restrict__ ids, int64_t n, int chunk, int expert_begin, int E, int* __restrict__ hist,
     int* __restrict__ ranks, SortLayout L) {
   extern __shared__ int smem[];
   int* tot = smem;                                             // [E]
   uint16_t* wc = reinterpret_cast<uint16_t*>(tot + E);         // [SORT_WAVES][E]
-  const int64_t base = (int64_t)blockIdx.x * MOE_SORT_CHUNK;
-  const int n_in = (int)(n - base < MOE_SORT_CHUNK ? n - base : MOE_SORT_CHUNK);
+  const int64_t base = (int64_t)blockIdx.x * chunk;
+  const int n_in = (int)(n - base < chunk ? n - base : chunk);
   int key[ROUNDS], rank[ROUNDS];
   rank_chunk(ids, base, n_in, expert_begin, E, wc, tot, key, rank);
   zero_sync(L, (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x, (int64_t)gridDim.x * SORT_THREADS);
@@ -350,22 +351,22 @@ __global__ __launch_bounds__(SCAN_THREADS) void sort_scan_kernel(int* __restrict
   if (threadIdx.x == 0) *L.num_tiles = total;
 }
 
-// Rows to their positions: SCATTER_SPLIT workgroups per chunk, each thread SCATTER_RPT rows with
-// all their loads issued together.  The row that opens a tile writes the tile's expert id, an
+// Rows to their positions: chunk / SCATTER_ROWS workgroups per chunk, each thread SCATTER_RPT
+// rows with all their loads issued together.  The row that opens a tile writes the tile's expert id, an
 // expert's last row writes the padding of its last tile, and all workgroups share the unused
 // tail (expert -1, sentinel rows).
 constexpr int SCATTER_THREADS = 256;
 constexpr int SCATTER_RPT = 4;
-constexpr int SCATTER_SPLIT = MOE_SORT_CHUNK / (SCATTER_THREADS * SCATTER_RPT);
-static_assert(SCATTER_SPLIT * SCATTER_THREADS * SCATTER_RPT == MOE_SORT_CHUNK, "whole chunks");
+constexpr int SCATTER_ROWS = SCATTER_THREADS * SCATTER_RPT;   // rows per workgroup
+static_assert(MOE_SORT_MIN_CHUNK % SCATTER_ROWS == 0 && MOE_SORT_CHUNK % MOE_SORT_MIN_CHUNK == 0, "whole chunks");
 
 __global__ __launch_bounds__(SCATTER_THREADS) void sort_scatter_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ topk_w, int64_t n, int expert_begin,
-    int E, int block_m, int nchunks, const int* __restrict__ hist, const int* __restrict__ ranks,
+    int E, int block_m, int nchunks, int chunk_rows, const int* __restrict__ hist, const int* __restrict__ ranks,
     SortLayout L) {
-  const int chunk = blockIdx.x / SCATTER_SPLIT;
-  const int64_t base = (int64_t)chunk * MOE_SORT_CHUNK +
-                       (int64_t)(blockIdx.x % SCATTER_SPLIT) * (SCATTER_THREADS * SCATTER_RPT);
+  const int split = chunk_rows / SCATTER_ROWS;
+  const int chunk = blockIdx.x / split;
+  const int64_t base = (int64_t)chunk * chunk_rows + (int64_t)(blockIdx.x % split) * SCATTER_ROWS;
   const int* first = hist + (int64_t)nchunks * E;
   const int* cnt = first + E;
   const int sentinel = (int)n;
@@ -436,19 +437,24 @@ hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, 
                                                               block_m, L);
     return hipGetLastError();
   }
-  const int nchunks = (int)((n + MOE_SORT_CHUNK - 1) / MOE_SORT_CHUNK);
+  // about 64 chunks: enough counting workgroups at 16k rows, few enough chunk offsets for the
+  // one-workgroup scan at 256k (sort µs at 16384 / 131072 / 262144 rows: 22.6 / 20.0 / 26.5 with
+  // 4096-row chunks, 18.0 / 20.0 / 37.4 with 1024, 19.4 / 18.6 / 28.3 with 2048)
+  const int chunk = n <= 64 * MOE_SORT_MIN_CHUNK ? MOE_SORT_MIN_CHUNK
+                    : n <= 64 * 2 * MOE_SORT_MIN_CHUNK ? 2 * MOE_SORT_MIN_CHUNK : MOE_SORT_CHUNK;
+  const int nchunks = (int)((n + chunk - 1) / chunk);
   int* hist = (int*)ws;
   int* ranks = (int*)((char*)ws + moe_align256((size_t)(nchunks + 2) * E * sizeof(int)));
   sort_count_kernel<<<nchunks, SORT_THREADS, (size_t)E * sizeof(int) + wc_bytes, s>>>(
-      topk_ids, n, expert_begin, E, hist, ranks, L);
+      topk_ids, n, chunk, expert_begin, E, hist, ranks, L);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scan_kernel<<<1, SCAN_THREADS, (size_t)(E + SCAN_THREADS / WAVE + 1) * sizeof(int), s>>>(
       hist, nchunks, E, block_m, L);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  sort_scatter_kernel<<<nchunks * SCATTER_SPLIT, SCATTER_THREADS, 0, s>>>(topk_ids, topk_w, n, expert_begin, E,
-                                                                        block_m, nchunks, hist, ranks, L);
+  sort_scatter_kernel<<<nchunks * (chunk / SCATTER_ROWS), SCATTER_THREADS, 0, s>>>(
+      topk_ids, topk_w, n, expert_begin, E, block_m, nchunks, chunk, hist, ranks, L);
   return hipGetLastError();
 }
 
