@@ -236,6 +236,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint, for the packed Stage1 weights: each instruction
+// copies whole 128-byte lines, which in most groups no other item reads (ldw16 has the
+// measurements).
+__device__ __forceinline__ void dma16nt(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
+}
+
 // 4 bytes per lane: global (base + off) -> LDS (lds + 4 * lane).
 __device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory", "m0");
@@ -499,7 +506,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
       if (i < q.n_ai) dma16(ab, q.a_off[i], L + (i * NLOAD + lw) * 1024);
 #pragma unroll
     for (int i = 0; i < F::B_IPL; ++i)
-      dma16(bb, q.b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
+      dma16nt(bb, q.b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
     if (AS1 && q.as_on) dma4(p.xs + s * 4, q.as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
   };
 

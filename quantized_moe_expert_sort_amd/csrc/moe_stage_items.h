@@ -161,7 +161,7 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     for (int i = 0; i < PF; ++i)
       if (FULL || s0 + i < s_end)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 1024);
+        for (int j = 0; j < NB; ++j) bq[i][j] = ldw16(bbase[j] + i * 1024);
     // every load of the chunk is issued before the first wait (the scheduler would otherwise
     // sink the later steps' loads below the first MFMAs, a second memory round trip)
     __builtin_amdgcn_sched_barrier(0);
@@ -239,7 +239,7 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
     for (int i = 0; i < PF; ++i)
       if (FULL || i < n_s)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[i][j] = ld16(bbase[j] + i * 1024);
+        for (int j = 0; j < NB; ++j) bq[i][j] = ldw16(bbase[j] + i * 1024);
     __builtin_amdgcn_sched_barrier(0);
     // the copies were issued before the PF*NB weight loads: once at most that many loads are
     // outstanding, the staged rows are in LDS
