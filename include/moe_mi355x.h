@@ -49,7 +49,11 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 2,   /* a shape or option the kernels do not implement */
   MOE_ERR_CAPACITY = 3,      /* layout capacity smaller than moe_cap_tiles() */
   MOE_ERR_HIP = 4,           /* a HIP launch failed */
-  MOE_ERR_WORKSPACE = 5      /* workspace smaller than the *_ws_bytes() helper requires */
+  MOE_ERR_WORKSPACE = 5,     /* workspace smaller than the *_ws_bytes() helper requires */
+  MOE_ERR_DEBUG_CHECK = 6    /* debug build only (libmoe_mi355x_debug.so, compiled with
+                                MOE_DEBUG_CHECKS): a device-side index check failed; the
+                                guarded accesses were skipped and the outputs are not valid.
+                                That build waits for the device at the end of every call. */
 } moe_status_t;
 
 typedef enum { MOE_DT_BF16 = 0, MOE_DT_FP8_E4M3 = 1, MOE_DT_FP4_E2M1 = 2 } moe_dtype_t;

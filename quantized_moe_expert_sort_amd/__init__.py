@@ -18,11 +18,14 @@ DTYPES = {"bf16": DT_BF16, "fp8": DT_FP8, "fp4": DT_FP4}
 ACTS = {"situv2": ACT_SITUV2, "silu": ACT_SILU, "none_test": ACT_NONE_TEST}
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_CAPACITY",
-          4: "MOE_ERR_HIP", 5: "MOE_ERR_WORKSPACE"}
+          4: "MOE_ERR_HIP", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_DEBUG_CHECK"}
 SORT_CHUNK = 4096
 SORT_MIN_CHUNK = 1024
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+# the same library built with MOE_DEBUG_CHECKS (device-side index checks; every call waits for
+# the device and returns MOE_ERR_DEBUG_CHECK when a check failed)
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x_debug.so")
 EXPORTS = ("moe_sort", "moe_quant_act", "moe_pack_w1", "moe_fused", "moe_fused_noalloc", "moe_last_hip_error")
 NOALLOC_SCRATCH_BYTES = 128 << 20
 
@@ -74,6 +77,14 @@ def lib():
         L.moe_last_hip_error.restype = i32
         _lib = L
     return _lib
+
+
+def select_library(path):
+    """Route later calls to the library at `path` (LIB_PATH or DEBUG_LIB_PATH); returns the
+    previous path."""
+    global LIB_PATH, _lib
+    prev, LIB_PATH, _lib = LIB_PATH, path, None
+    return prev
 
 
 def _check(fn, status):

@@ -1,4 +1,6 @@
-"""Build libmoe_mi355x.so (HIP for gfx950) in-tree: python -m quantized_moe_expert_sort_amd.build"""
+"""Build libmoe_mi355x.so (HIP for gfx950) in-tree, and its debug variant libmoe_mi355x_debug.so
+(the same sources with MOE_DEBUG_CHECKS: device-side index checks, every call waits for the
+device): python -m quantized_moe_expert_sort_amd.build"""
 import concurrent.futures
 import glob
 import os
@@ -10,6 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
+DEBUG_LIB = os.path.join(PKG, "libmoe_mi355x_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -20,28 +23,36 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(job):
+    src, outdir, extra = job
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    dbg = os.path.join(BUILD, "debug")
+    os.makedirs(dbg, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = [(s, BUILD, []) for s in srcs] + [(s, dbg, ["-DMOE_DEBUG_CHECKS"]) for s in srcs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {DEBUG_LIB}")
     return LIB
 
 

@@ -3,6 +3,7 @@
 // thread-local copy of the last HIP error, and for moe_fused_noalloc the per-device address of
 // the library's fixed scratch array (taken once per device).
 #include <cmath>
+#include <cstdio>
 #include <mutex>
 
 #include "moe_kernels.h"
@@ -50,6 +51,29 @@ moe_status_t hip_status(hipError_t e) {
   return MOE_ERR_HIP;
 }
 
+// The debug build (MOE_DEBUG_CHECKS) ends every launching call by waiting for the device and
+// collecting the kernels' violation words; the normal build returns the launch status as is.
+moe_status_t finish(moe_status_t st) {
+#ifdef MOE_DEBUG_CHECKS
+  if (st != MOE_OK) return st;
+  hipError_t e = hipDeviceSynchronize();
+  uint32_t bits = 0;
+  hipError_t (*const take[])(uint32_t*) = {moe::debug_take_sort, moe::debug_take_gemm, moe::debug_take_grouped,
+                                           moe::debug_take_single};
+  for (auto f : take) {
+    uint32_t v = 0;
+    if (e == hipSuccess) e = f(&v);
+    bits |= v;
+  }
+  if (e != hipSuccess) return hip_status(e);
+  if (bits) {
+    fprintf(stderr, "libmoe_mi355x_debug: device index check failed (bits 0x%x)\n", bits);
+    return MOE_ERR_DEBUG_CHECK;
+  }
+#endif
+  return st;
+}
+
 bool valid_dtype(int32_t dt) { return dt == MOE_DT_BF16 || dt == MOE_DT_FP8_E4M3 || dt == MOE_DT_FP4_E2M1; }
 
 moe_status_t check_layout(const moe_layout_t* L, int32_t tokens, int32_t topk, int32_t E) {
@@ -84,8 +108,8 @@ moe_status_t moe_sort(const int32_t* topk_ids, const float* topk_w, int32_t toke
                     layout->num_tiles, layout->row_of, layout->sync,
                     layout->sync ? (int64_t)moe_sync_words(tokens, layout->cap_tiles) : 0,
                     layout->cap_tiles};
-  return hip_status(moe::launch_sort(topk_ids, topk_w, n, expert_begin, num_local_experts,
-                                     layout->block_m, L, ws, (hipStream_t)stream));
+  return finish(hip_status(moe::launch_sort(topk_ids, topk_w, n, expert_begin, num_local_experts,
+                                            layout->block_m, L, ws, (hipStream_t)stream)));
 }
 
 moe_status_t moe_pack_w1(const uint8_t* w1, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
@@ -98,7 +122,7 @@ moe_status_t moe_pack_w1(const uint8_t* w1, int32_t num_experts, int32_t model_d
   const uintptr_t bytes = (uintptr_t)num_experts * 2 * (uintptr_t)inter_dim * (uintptr_t)(model_dim / 2);
   const uintptr_t a = (uintptr_t)w1, b = (uintptr_t)w1_packed;
   if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_pack_w1(w1, w1_packed, num_experts, model_dim, inter_dim, (hipStream_t)stream));
+  return finish(hip_status(moe::launch_pack_w1(w1, w1_packed, num_experts, model_dim, inter_dim, (hipStream_t)stream)));
 }
 
 moe_status_t moe_quant_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, int32_t dt, void* q_out,
@@ -107,7 +131,7 @@ moe_status_t moe_quant_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, i
   if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
   if (!x_bf16 || !q_out || !scale_out) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_quant_act(x_bf16, rows, cols, dt, q_out, scale_out, (hipStream_t)stream));
+  return finish(hip_status(moe::launch_quant_act(x_bf16, rows, cols, dt, q_out, scale_out, (hipStream_t)stream)));
 }
 
 }  // extern "C"
@@ -202,8 +226,8 @@ moe_status_t fused_call(const void* x, const uint8_t* x_scale, int32_t a_dtype, 
   a.stages = stages;
   if (layout->sync && tokens < MOE_SINGLE_LAUNCH_MAX_TOKENS && stages == MOE_STAGE_ALL &&
       act->act != MOE_ACT_NONE_TEST)
-    return hip_status(moe::launch_single(a, (hipStream_t)stream));
-  return hip_status(moe::launch_fused(a, (hipStream_t)stream));
+    return finish(hip_status(moe::launch_single(a, (hipStream_t)stream)));
+  return finish(hip_status(moe::launch_fused(a, (hipStream_t)stream)));
 }
 
 }  // namespace

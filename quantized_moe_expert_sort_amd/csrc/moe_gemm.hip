@@ -63,7 +63,8 @@ template <bool W = false>
 __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restrict__ rowout,
                                                           const int32_t* __restrict__ row_of,
                                                           uint16_t* __restrict__ out, int T, int topk,
-                                                          int D, const float* __restrict__ topk_w = nullptr,
+                                                          int D, int64_t n_rows,
+                                                          const float* __restrict__ topk_w = nullptr,
                                                           const int32_t* __restrict__ hot_e = nullptr,
                                                           const uint32_t* __restrict__ hotmask = nullptr,
                                                           const uint8_t* __restrict__ hot_out = nullptr) {
@@ -92,6 +93,9 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const uint8_t* __restr
 #pragma unroll
     for (int u = 0; u < KG; ++u)
       r[u] = k0 + u < topk && !((hmask >> (k0 + u)) & 1u) ? row_of[(int64_t)t * topk + k0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < KG; ++u)
+      if (!MOE_DCHECK(r[u] >= -1 && r[u] < n_rows, DBG_COMBINE_ROW)) r[u] = -1;
     uint4 q[KG];
     float wk[KG];
 #pragma unroll
@@ -187,7 +191,10 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_small_kernel(FusedArgs p) {
     const int tile = min(wave + SMALL_WAVES * q, p.cap_tiles - 1);
     eid[q] = p.expert_ids[tile];
 #pragma unroll
-    for (int f = 0; f < MF; ++f) vr[q][f] = p.sorted_ids[tile * BM + 16 * f + r16];
+    for (int f = 0; f < MF; ++f) {
+      vr[q][f] = p.sorted_ids[tile * BM + 16 * f + r16];
+      dcheck_row_id(vr[q][f], TK);
+    }
   }
   if ((int)threadIdx.x < NR) written[threadIdx.x] = 0;
   if ((int)threadIdx.x < SB / 4) reinterpret_cast<uint32_t*>(zero_step)[threadIdx.x] = 0u;
@@ -406,12 +413,13 @@ hipError_t run_stages(FusedArgs a, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   const int64_t nthreads = (int64_t)a.T * (a.D / 8);
+  const int64_t n_rows = (int64_t)a.cap_tiles * a.block_m;
   const unsigned gridc = (unsigned)((nthreads + THREADS - 1) / THREADS);
   if (tiled2)   // grouped Stage2 rows carry no router weight
-    combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, a.topk_w,
+    combine_kernel<true><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, n_rows, a.topk_w,
                                                    hot_path(a) ? a.hot_e : nullptr, a.hotmask, a.hot_out);
   else
-    combine_kernel<false><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D);
+    combine_kernel<false><<<gridc, THREADS, 0, s>>>(a.rowout, a.row_of, a.out, a.T, a.topk, a.D, n_rows);
   return hipGetLastError();
 }
 
@@ -427,5 +435,7 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t s) {
          : a.a_dtype == DT_FP8 ? run_dtype<DT_FP8>(a, s)
                                : run_dtype<DT_FP4>(a, s);
 }
+
+MOE_DEBUG_READER(gemm)
 
 }  // namespace moe

@@ -407,6 +407,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
     const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
     tile0 = ld_const(gp);
     ntile = ld_const(gp + 1);
+    if (!MOE_DCHECK(tile0 >= 0 && ntile >= 0 && tile0 + ntile <= p.cap_tiles, DBG_GROUP)) tile0 = ntile = 0;
     if (PARTS == 2) {
       const int h0 = ntile <= F::GTA ? ntile : (ntile + 1) >> 1;
       tile0 += part ? h0 : 0;
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
     q.rows_used = ntile * 32;
     q.row_base = tile0 * 32;
     if (!loader) return;
-    const int e = ld_const(p.expert_ids + tile0);
+    const int e = dcheck_expert(ld_const(p.expert_ids + tile0), p.E);
     q.b = p.w1 + (size_t)e * 2 * I * (D / 2);
     q.bs = p.w1s + (size_t)e * 2 * I * (D / 32);
     auto b_row = [&](int r) -> int {                      // weight row within the expert
@@ -463,6 +464,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage1_kernel(FusedArgs p
     for (int i = 0; i < F::A_IPL; ++i)
       rid[i] = p.sorted_ids[q.row_base + min(((i * NLOAD + lw) * WAVE + ln) / ACPR, q.rows_used - 1)];
     rid[F::A_IPL] = p.sorted_ids[q.row_base + min(sc_row, q.rows_used - 1)];
+#pragma unroll
+    for (int i = 0; i <= F::A_IPL; ++i) dcheck_row_id(rid[i], TK);
     auto tok = [&](int row, int v) -> uint32_t {          // token row of A row `row`
       return (uint32_t)(row < q.rows_used && (unsigned)v < (unsigned)TK ? v / p.topk : 0);
     };
@@ -844,6 +847,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
     q.nb = rem - gl * n_nblk;
     const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
     int tile0 = ld_const(gp), ntiles = ld_const(gp + 1);
+    if (!MOE_DCHECK(tile0 >= 0 && ntiles >= 0 && tile0 + ntiles <= p.cap_tiles, DBG_GROUP)) tile0 = ntiles = 0;
     if (PARTS == 2) {
       const int h0 = ntiles <= F::GTA ? ntiles : (ntiles + 1) >> 1;
       tile0 += part ? h0 : 0;
@@ -851,7 +855,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
     }
     q.rows_used = ntiles * 32;
     q.row_base = tile0 * 32;
-    const int e = ld_const(p.expert_ids + tile0);
+    const int e = dcheck_expert(ld_const(p.expert_ids + tile0), p.E);
     q.a = p.inter + (size_t)q.row_base * a_rowbytes;
     q.as = p.inter_s + (size_t)q.row_base * (I / 32);
     q.b = p.w2 + (size_t)e * D * (I / 2);
@@ -1140,6 +1144,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedAr
     const int gl = rem / n_rng, rg = rem - gl * n_rng;
     const int32_t* gp = reinterpret_cast<const int32_t*>(groups + gl * 8 + xcd);
     int tile0 = ld_const(gp), ntiles = ld_const(gp + 1);
+    if (!MOE_DCHECK(tile0 >= 0 && ntiles >= 0 && tile0 + ntiles <= p.cap_tiles, DBG_GROUP)) tile0 = ntiles = 0;
     if (PARTS == 2) {
       const int h0 = ntiles <= F::GTA ? ntiles : (ntiles + 1) >> 1;
       tile0 += part ? h0 : 0;
@@ -1148,7 +1153,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedAr
     const int cb0 = rg * n_nblk / n_rng, cb1 = (rg + 1) * n_nblk / n_rng;
     if (ntiles == 0 || cb0 == cb1) continue;             // the empty second part of a small group
     const int rows_used = ntiles * 32, row_base = tile0 * 32;
-    const int e = ld_const(p.expert_ids + tile0);
+    const int e = dcheck_expert(ld_const(p.expert_ids + tile0), p.E);
     const uint8_t* qa = p.inter + (size_t)row_base * a_rowbytes;
     const uint8_t* qas = p.inter_s + (size_t)row_base * (I / 32);
     const uint8_t* qb = p.w2 + (size_t)e * D * (I / 2);
@@ -1726,5 +1731,7 @@ hipError_t launch_tiled(const FusedArgs& a, int2* groups, int32_t* ngroups, hipS
   }
   return hipSuccess;
 }
+
+MOE_DEBUG_READER(grouped)
 
 }  // namespace moe

@@ -21,6 +21,47 @@ struct SortLayout {
 
 constexpr int MAX_SORT_EXPERTS = MOE_SORT_MAX_EXPERTS;
 
+// ---------------------------------------------------------------- debug checks
+//
+// Built with -DMOE_DEBUG_CHECKS (the separate library libmoe_mi355x_debug.so), the kernels check
+// index invariants they otherwise take from the sort and the host checks: the positions the
+// sort writes, the row ids and expert ids the stages read from the layout, the tile ranges of
+// the grouped stages and the rows the combine gathers.  A failed check does not trap: it sets
+// its bit in the violation word of its source file and the access it guards is skipped (a row
+// id outside the layout reads as padding), so the launch ends normally.  Every entry point of
+// the debug library then waits for the device, collects and clears the words and returns
+// MOE_ERR_DEBUG_CHECK if a bit was set.  In the normal build MOE_DCHECK is `true` and adds no
+// code.
+enum : uint32_t {
+  DBG_SORT_POS = 1u,      // a sorted position past cap_tiles * block_m
+  DBG_LAYOUT_ROW = 2u,    // a layout row id outside [0, T*topk] (T*topk marks padding)
+  DBG_EXPERT = 4u,        // a tile's expert id >= num_local_experts
+  DBG_GROUP = 8u,         // a tile group outside [0, cap_tiles)
+  DBG_COMBINE_ROW = 16u,  // a row_of entry outside [-1, cap_tiles * block_m)
+};
+#ifdef MOE_DEBUG_CHECKS
+static __device__ uint32_t dbg_word;   // one per source file
+#define MOE_DCHECK(cond, bit) ((cond) ? true : (atomicOr(&::moe::dbg_word, (uint32_t)(bit)), false))
+// host side: the word of one source file, cleared after it is read
+#define MOE_DEBUG_READER(name)                                                         \
+  hipError_t debug_take_##name(uint32_t* v) {                                          \
+    const uint32_t z = 0;                                                              \
+    hipError_t e = hipMemcpyFromSymbol(v, HIP_SYMBOL(dbg_word), sizeof(uint32_t));     \
+    return e != hipSuccess ? e : hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), &z, sizeof(uint32_t)); \
+  }
+hipError_t debug_take_sort(uint32_t* v);
+hipError_t debug_take_gemm(uint32_t* v);
+hipError_t debug_take_grouped(uint32_t* v);
+hipError_t debug_take_single(uint32_t* v);
+#else
+#define MOE_DCHECK(cond, bit) true
+#define MOE_DEBUG_READER(name)
+#endif
+// a layout row id (T*topk marks padding; the stages read anything else as padding too)
+__device__ __forceinline__ void dcheck_row_id(int v, int TK) { (void)MOE_DCHECK((unsigned)v <= (unsigned)TK, DBG_LAYOUT_ROW); }
+// a tile's expert id for a weight address: -1 never reaches here; an id past E reads expert 0
+__device__ __forceinline__ int dcheck_expert(int e, int E) { return MOE_DCHECK((unsigned)e < (unsigned)E, DBG_EXPERT) ? e : 0; }
+
 hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, int expert_begin,
                        int E, int block_m, const SortLayout& L, void* ws, hipStream_t s);
 

@@ -171,4 +171,6 @@ hipError_t launch_single(const FusedArgs& a, hipStream_t s) {
                                : run_dtype<DT_FP4>(a, s);
 }
 
+MOE_DEBUG_READER(single)
+
 }  // namespace moe

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(WAVE) void sort_wave_kernel(const int32_t* __restri
   }
   const int sentinel = n;
   const int p = off * block_m + rank;
-  if (valid) {
+  if (valid && MOE_DCHECK((int64_t)p < L.cap_tiles * block_m, DBG_SORT_POS)) {
     L.sorted_ids[p] = lane;
     if (L.sorted_w) L.sorted_w[p] = w;
   }
@@ -259,6 +259,7 @@ __global__ __launch_bounds__(SORT_THREADS) void sort_small_kernel(
     }
     const int q = rank[r];                                     // rank within the expert
     const int f = first[k], p = f + q;
+    if (!MOE_DCHECK((int64_t)p < L.cap_tiles * block_m, DBG_SORT_POS)) continue;
     L.sorted_ids[p] = v;
     if (L.sorted_w) L.sorted_w[p] = topk_w[v];
     if (L.row_of) L.row_of[v] = p;
@@ -399,6 +400,7 @@ __global__ __launch_bounds__(SCATTER_THREADS) void sort_scatter_kernel(
     }
     const int q = h[u] + r[u];                            // rank within the expert
     const int p = f[u] + q;
+    if (!MOE_DCHECK((int64_t)p < L.cap_tiles * block_m, DBG_SORT_POS)) continue;
     L.sorted_ids[p] = (int32_t)v;
     if (L.sorted_w) L.sorted_w[p] = w[u];
     if (L.row_of) L.row_of[v] = p;
@@ -457,5 +459,7 @@ hipError_t launch_sort(const int32_t* topk_ids, const float* topk_w, int64_t n, 
       topk_ids, topk_w, n, expert_begin, E, block_m, nchunks, chunk, hist, ranks, L);
   return hipGetLastError();
 }
+
+MOE_DEBUG_READER(sort)
 
 }  // namespace moe

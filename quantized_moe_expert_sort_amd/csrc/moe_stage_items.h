@@ -96,7 +96,12 @@ __device__ __forceinline__ bool stage1_item(const FusedArgs& p, int tile, int nb
 #pragma unroll
   for (int f = 0; f < MF; ++f) vr[f] = p.sorted_ids[tile * BM + 16 * f + r16];
   const int e = p.expert_ids[tile];
-  if (e < 0 || e >= p.E) return false;
+  if (e < 0 || e >= p.E) {
+    (void)MOE_DCHECK(e < p.E, DBG_EXPERT);   // -1 marks an unused tile
+    return false;
+  }
+#pragma unroll
+  for (int f = 0; f < MF; ++f) dcheck_row_id(vr[f], TK);
 
   const size_t a_row = (size_t)D * row_bytes_num<ADT>() / row_bytes_den<ADT>();
   const uint8_t* arow[MF];
@@ -388,7 +393,12 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
 #pragma unroll
     for (int i = 0; i < 4; ++i) vrow[f][i] = p.sorted_ids[tile * BM + 16 * f + 4 * g + i];
   const int e = p.expert_ids[tile];
-  if (e < 0 || e >= p.E) return false;
+  if (e < 0 || e >= p.E) {
+    (void)MOE_DCHECK(e < p.E, DBG_EXPERT);
+    return false;
+  }
+#pragma unroll
+  for (int f = 0; f < MF; ++f) dcheck_row_id(vr[f], TK);
   // router weights of the accumulator rows, requested before the operands
   float wrow[MF][4];
 #pragma unroll
@@ -571,7 +581,10 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
 template <int KG>
 __device__ __forceinline__ void token_rows(const FusedArgs& p, int t, int k0, int (&r)[KG]) {
 #pragma unroll
-  for (int u = 0; u < KG; ++u) r[u] = k0 + u < p.topk ? p.row_of[(int64_t)t * p.topk + k0 + u] : -1;
+  for (int u = 0; u < KG; ++u) {
+    r[u] = k0 + u < p.topk ? p.row_of[(int64_t)t * p.topk + k0 + u] : -1;
+    if (!MOE_DCHECK(r[u] >= -1 && (int64_t)r[u] < (int64_t)p.cap_tiles * p.block_m, DBG_COMBINE_ROW)) r[u] = -1;
+  }
 }
 
 // Two neighbouring columns c, c+1 of routed row r (0 where r < 0).
