@@ -21,11 +21,12 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
   }
 }
 
-// 16 bytes of a weight stream that is read once per launch in whole 128-byte lines (the packed
-// Stage1 weights: one load instruction of a wave covers a contiguous 1 KB block), with the
-// non-temporal hint.  On an MI355X a plain streaming read of 2 GiB ran at 7.0-7.2 TB/s with the
-// hint and 6.1-6.2 TB/s without it.  Not for data whose lines are split between two load
-// instructions (the 192-byte row-major Stage2 weight rows): there the hint made Stage2 slower.
+// 16 bytes of a stream that is read once per launch in whole 128-byte lines (one load
+// instruction of a wave covers a contiguous 1 KB: the packed Stage1 weights, the per-row Stage2
+// outputs the combine sums), with the non-temporal hint.  On an MI355X a plain streaming read of
+// 2 GiB ran at 7.0-7.2 TB/s with the hint and 6.1-6.2 TB/s without it.  Not for data whose lines
+// are split between two load instructions (the 192-byte row-major Stage2 weight rows): there the
+// hint made Stage2 slower.
 __device__ __forceinline__ uint4 ldw16(const uint8_t* p) {
   typedef uint32_t u4v_ __attribute__((ext_vector_type(4)));
   const u4v_ v = __builtin_nontemporal_load(reinterpret_cast<const u4v_*>(p));

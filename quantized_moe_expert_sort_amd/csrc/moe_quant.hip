@@ -7,6 +7,7 @@
 // first lane of a block writes the scale byte.
 #include "moe_kernels.h"
 #include "moe_device.h"
+#include "moe_operands.h"
 
 namespace moe {
 
@@ -17,7 +18,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nocts; i += stride) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + i * 8);
+    const uint4 raw = ldw16(reinterpret_cast<const uint8_t*>(x + i * 8));   // read once: non-temporal
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     float v[8];
     uint32_t amax = 0;
