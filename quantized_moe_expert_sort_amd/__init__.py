@@ -13,7 +13,7 @@ import torch
 DT_BF16, DT_FP8, DT_FP4 = 0, 1, 2
 ACT_SITUV2, ACT_SILU, ACT_NONE_TEST = 0, 1, 2
 STAGE_1, STAGE_2, STAGE_ALL = 1, 2, 3
-W1_ROW_MAJOR, W1_PACKED = 0, 1
+W_ROW_MAJOR, W1_PACKED, W_PACKED = 0, 1, 2
 DTYPES = {"bf16": DT_BF16, "fp8": DT_FP8, "fp4": DT_FP4}
 ACTS = {"situv2": ACT_SITUV2, "silu": ACT_SILU, "none_test": ACT_NONE_TEST}
 
@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 # the same library built with MOE_DEBUG_CHECKS (device-side index checks; every call waits for
 # the device and returns MOE_ERR_DEBUG_CHECK when a check failed)
 DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x_debug.so")
-EXPORTS = ("moe_sort", "moe_quant_act", "moe_pack_w1", "moe_fused", "moe_fused_noalloc", "moe_last_hip_error")
+EXPORTS = ("moe_sort", "moe_quant_act", "moe_pack_w1", "moe_pack_w2", "moe_fused", "moe_fused_noalloc",
+           "moe_last_hip_error")
 NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
@@ -73,6 +74,8 @@ def lib():
         L.moe_fused_noalloc.restype = i32
         L.moe_pack_w1.argtypes = [vp, i32, i32, i32, vp, vp]
         L.moe_pack_w1.restype = i32
+        L.moe_pack_w2.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.moe_pack_w2.restype = i32
         L.moe_last_hip_error.argtypes = []
         L.moe_last_hip_error.restype = i32
         _lib = L
@@ -221,12 +224,22 @@ def moe_pack_w1(w1, out=None):
     return out
 
 
+def moe_pack_w2(w2, out=None):
+    """Stage2 weights [E, D, I/2] uint8 (row-major) -> the packed layout moe_fused reads."""
+    E, D, half_i = w2.shape
+    if out is None:
+        out = torch.empty_like(w2)
+    _check("moe_pack_w2", lib().moe_pack_w2(_ptr(w2), E, D, half_i * 2, _ptr(out), _stream()))
+    return out
+
+
 def device_weights(w1, w1s, w2, w2s, device="cuda"):
-    """Host MXFP4 weights (numpy, row-major) -> the device tuple moe_fused takes (w1 packed)."""
+    """Host MXFP4 weights (numpy, row-major) -> the device tuple moe_fused takes (w1 and w2
+    packed, the scales as they are)."""
     w1_d, w1s_d, w2_d, w2s_d = (torch.from_numpy(a).to(device) for a in (w1, w1s, w2, w2s))
-    packed = moe_pack_w1(w1_d)
-    del w1_d
-    return packed, w1s_d, w2_d, w2s_d
+    p1, p2 = moe_pack_w1(w1_d), moe_pack_w2(w2_d)
+    del w1_d, w2_d
+    return p1, w1s_d, p2, w2s_d
 
 
 def moe_quant_act(x_bf16, dt, q=None, scale=None):
@@ -243,10 +256,11 @@ def moe_quant_act(x_bf16, dt, q=None, scale=None):
 
 def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, num_local_experts,
               act="situv2", beta=None, linear_beta=None, out=None, ws=None, stages=STAGE_ALL,
-              w1_layout=W1_PACKED):
+              w_layout=W_PACKED):
     """Stage1 + Stage2 over a layout from moe_sort; returns out [T, D] bf16 (or, for
-    act="none_test", the workspace tensor holding the raw gate/up sums).  w1 is in the layout
-    named by w1_layout (the library reads W1_PACKED, as moe_pack_w1 writes it).  stages selects
+    act="none_test", the workspace tensor holding the raw gate/up sums).  w1 and w2 are in the
+    layout named by w_layout (the library reads W_PACKED, as moe_pack_w1 / moe_pack_w2 write
+    them; device_weights does both).  stages selects
     STAGE_1, STAGE_2 (reusing the intermediate a STAGE_1 call left in the same ws) or both."""
     d = DTYPES[a_dtype] if isinstance(a_dtype, str) else a_dtype
     a = ACTS[act] if isinstance(act, str) else act
@@ -261,7 +275,7 @@ def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, n
                          device=topk_w.device)
     if out is None and a != ACT_NONE_TEST:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=topk_w.device)
-    _check("moe_fused", lib().moe_fused(_ptr(x), _ptr(x_scale), d, _ptr(w1), w1_layout, _ptr(w1_scale), _ptr(w2),
+    _check("moe_fused", lib().moe_fused(_ptr(x), _ptr(x_scale), d, _ptr(w1), w_layout, _ptr(w1_scale), _ptr(w2),
                                         _ptr(w2_scale), _ptr(topk_w), ctypes.byref(layout.c), T, K,
                                         num_local_experts, D, I, ctypes.byref(params), _ptr(out),
                                         _ptr(ws), ws.numel(), stages, _stream()))
@@ -270,7 +284,7 @@ def moe_fused(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, n
 
 def moe_fused_noalloc(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, layout, num_local_experts,
                       act="situv2", beta=None, linear_beta=None, out=None, stages=STAGE_ALL,
-                      w1_layout=W1_PACKED):
+                      w_layout=W_PACKED):
     """moe_fused with the library's fixed per-device scratch as its workspace (nothing allocated
     for the workspace; calls on one device share it and must not overlap).  Returns out."""
     d = DTYPES[a_dtype] if isinstance(a_dtype, str) else a_dtype
@@ -283,7 +297,7 @@ def moe_fused_noalloc(x, x_scale, a_dtype, w1, w1_scale, w2, w2_scale, topk_w, l
     params = ActParams(a, 0.0 if beta is None else beta, 0.0 if linear_beta is None else linear_beta)
     if out is None and a != ACT_NONE_TEST:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=topk_w.device)
-    _check("moe_fused_noalloc", lib().moe_fused_noalloc(_ptr(x), _ptr(x_scale), d, _ptr(w1), w1_layout,
+    _check("moe_fused_noalloc", lib().moe_fused_noalloc(_ptr(x), _ptr(x_scale), d, _ptr(w1), w_layout,
                                                         _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(topk_w),
                                                         ctypes.byref(layout.c), T, K, num_local_experts, D, I,
                                                         ctypes.byref(params), _ptr(out), stages, _stream()))

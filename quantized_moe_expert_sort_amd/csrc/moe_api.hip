@@ -112,17 +112,41 @@ moe_status_t moe_sort(const int32_t* topk_ids, const float* topk_w, int32_t toke
                                             layout->block_m, L, ws, (hipStream_t)stream)));
 }
 
-moe_status_t moe_pack_w1(const uint8_t* w1, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
-                         uint8_t* w1_packed, void* stream) {
-  if (!w1 || !w1_packed) return MOE_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// moe_pack_w1 and moe_pack_w2: the same checks on `rows_per_expert` rows of `k` fp4 values (w1:
+// 2I rows of D, w2: D rows of I); the copy reads w and writes w_packed in a different order, so
+// the two byte ranges must be disjoint.
+moe_status_t check_pack(const uint8_t* w, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
+                        const uint8_t* w_packed, int64_t rows_per_expert, int64_t k) {
+  if (!w || !w_packed) return MOE_ERR_INVALID_ARG;
   if (num_experts < 1 || model_dim <= 0 || inter_dim <= 0) return MOE_ERR_INVALID_ARG;
   if (model_dim % 128 != 0 || inter_dim % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)num_experts * 2 * inter_dim * (model_dim / 2) / 16 >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
-  // the copy reads w1 and writes w1_packed in a different order: the two ranges must be disjoint
-  const uintptr_t bytes = (uintptr_t)num_experts * 2 * (uintptr_t)inter_dim * (uintptr_t)(model_dim / 2);
-  const uintptr_t a = (uintptr_t)w1, b = (uintptr_t)w1_packed;
+  if ((int64_t)num_experts * rows_per_expert * (k / 2) / 16 >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  const uintptr_t bytes = (uintptr_t)num_experts * (uintptr_t)rows_per_expert * (uintptr_t)(k / 2);
+  const uintptr_t a = (uintptr_t)w, b = (uintptr_t)w_packed;
   if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_pack_w1(const uint8_t* w1, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
+                         uint8_t* w1_packed, void* stream) {
+  const moe_status_t st = check_pack(w1, num_experts, model_dim, inter_dim, w1_packed, 2 * (int64_t)inter_dim, model_dim);
+  if (st != MOE_OK) return st;
   return finish(hip_status(moe::launch_pack_w1(w1, w1_packed, num_experts, model_dim, inter_dim, (hipStream_t)stream)));
+}
+
+moe_status_t moe_pack_w2(const uint8_t* w2, int32_t num_experts, int32_t model_dim, int32_t inter_dim,
+                         uint8_t* w2_packed, void* stream) {
+  const moe_status_t st = check_pack(w2, num_experts, model_dim, inter_dim, w2_packed, model_dim, inter_dim);
+  if (st != MOE_OK) return st;
+  return finish(hip_status(moe::launch_pack_w2(w2, w2_packed, num_experts, model_dim, inter_dim, (hipStream_t)stream)));
 }
 
 moe_status_t moe_quant_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, int32_t dt, void* q_out,
@@ -141,14 +165,14 @@ namespace {
 // moe_fused and moe_fused_noalloc: the same validation and launches; the no-alloc variant takes
 // its workspace from the scratch array (scratch == true; ws and ws_bytes are ignored).
 moe_status_t fused_call(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
-                        int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                        int32_t w_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
                         const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
                         int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
                         const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
                         int32_t stages, void* stream, bool use_scratch) {
   if (!valid_dtype(a_dtype)) return MOE_ERR_INVALID_ARG;
-  if (w1_layout != MOE_W1_PACKED && w1_layout != MOE_W1_ROW_MAJOR) return MOE_ERR_INVALID_ARG;
-  if (w1_layout != MOE_W1_PACKED) return MOE_ERR_UNSUPPORTED;   // the kernels stream packed blocks only
+  if (w_layout != MOE_W_PACKED && w_layout != MOE_W1_PACKED && w_layout != MOE_W_ROW_MAJOR) return MOE_ERR_INVALID_ARG;
+  if (w_layout != MOE_W_PACKED) return MOE_ERR_UNSUPPORTED;   // the kernels stream packed blocks only
   if (stages != MOE_STAGE_1 && stages != MOE_STAGE_2 && stages != MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
   if (!act) return MOE_ERR_INVALID_ARG;
   if (act->act != MOE_ACT_SITUV2 && act->act != MOE_ACT_SILU && act->act != MOE_ACT_NONE_TEST)
@@ -235,22 +259,22 @@ moe_status_t fused_call(const void* x, const uint8_t* x_scale, int32_t a_dtype, 
 extern "C" {
 
 moe_status_t moe_fused(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
-                       int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                       int32_t w_layout, const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
                        const float* topk_w, const moe_layout_t* layout, int32_t tokens, int32_t topk,
                        int32_t num_local_experts, int32_t model_dim, int32_t inter_dim,
                        const moe_act_params_t* act, uint16_t* out_bf16, void* ws, size_t ws_bytes,
                        int32_t stages, void* stream) {
-  return fused_call(x, x_scale, a_dtype, w1, w1_layout, w1_scale, w2, w2_scale, topk_w, layout, tokens, topk,
+  return fused_call(x, x_scale, a_dtype, w1, w_layout, w1_scale, w2, w2_scale, topk_w, layout, tokens, topk,
                     num_local_experts, model_dim, inter_dim, act, out_bf16, ws, ws_bytes, stages, stream, false);
 }
 
 moe_status_t moe_fused_noalloc(const void* x, const uint8_t* x_scale, int32_t a_dtype, const uint8_t* w1,
-                               int32_t w1_layout, const uint8_t* w1_scale, const uint8_t* w2,
+                               int32_t w_layout, const uint8_t* w1_scale, const uint8_t* w2,
                                const uint8_t* w2_scale, const float* topk_w, const moe_layout_t* layout,
                                int32_t tokens, int32_t topk, int32_t num_local_experts, int32_t model_dim,
                                int32_t inter_dim, const moe_act_params_t* act, uint16_t* out_bf16,
                                int32_t stages, void* stream) {
-  return fused_call(x, x_scale, a_dtype, w1, w1_layout, w1_scale, w2, w2_scale, topk_w, layout, tokens, topk,
+  return fused_call(x, x_scale, a_dtype, w1, w_layout, w1_scale, w2, w2_scale, topk_w, layout, tokens, topk,
                     num_local_experts, model_dim, inter_dim, act, out_bf16, nullptr, 0, stages, stream, true);
 }
 

@@ -257,10 +257,10 @@ __global__ __launch_bounds__(NW * WAVE) void stage2_small_kernel(FusedArgs p) {
     }
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
-      const uint8_t* brow = p.w2 + ((size_t)ew[q] * D + nb * 16 + r16) * (I / 2) + 16 * g;
+      const uint8_t* brow = p.w2 + ((size_t)ew[q] * D + nb * 16) * (I / 2) + 16 * lane;   // packed w2
 #pragma unroll
       for (int i = 0; i < SMALL_PS; ++i)
-        if (FULL || i < n_s) bq[q][i] = ld16(brow + (s0 + i) * 64);
+        if (FULL || i < n_s) bq[q][i] = ldw16(brow + (s0 + i) * 1024);
     }
     __builtin_amdgcn_sched_barrier(0);
     auto tile_mfmas = [&](int q) {

@@ -20,9 +20,10 @@
 // so the only waits on them are the explicit vmcnt waits of the pipeline.  The 16-byte chunks
 // of an activation / intermediate row and of a Stage2 weight row are stored XOR-swizzled (chunk
 // p of row r at position p ^ swz(r)), so the 16 lanes that read one chunk column of 16 rows for
-// a matrix-core operand hit distinct LDS banks.  Stage1 weights arrive packed (moe_pack.hip):
-// one copy instruction moves a whole 1 KB block (16 rows x one K step, already in lane order),
-// so a lane group's operand read is 256 consecutive bytes.
+// a matrix-core operand hit distinct LDS banks.  The weights arrive packed (moe_pack.hip): one
+// copy instruction moves a whole 1 KB block (16 rows x one K step); Stage1 keeps the block in
+// lane order, so a lane group's operand read is 256 consecutive bytes, and Stage2 has each lane
+// fetch the 16-byte piece of the block that its swizzled LDS position holds.
 //
 // The grid is persistent: one workgroup per CU, each looping over work items.  Groups are
 // dealt to the 8 XCDs round robin (workgroup b runs on XCD b % 8) and the column blocks of a
@@ -838,7 +839,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
     bool as_on, b_on;
   };
   // copy sources of item `local`: A the group's intermediate rows (rows past the group read its
-  // first row; their results are not stored), B output rows [nb*BNW, nb*BNW + BNW) of w2
+  // first row; their results are not stored), B output rows [nb*BNW, nb*BNW + BNW) of packed
+  // w2 (16 rows x one K step per 1 KB block: piece (row r, chunk p) at 16 (16 p + r % 16))
   // (bf16: a group of up to GTA tiles is one part, a larger one two parts of ceil(n/2) and
   // floor(n/2) tiles; the empty second part of a small group copies nothing)
   auto make = [&](int local, Src& q) {
@@ -874,7 +876,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
       const int j = i * NLOAD + lw;
       const int qq = j * WAVE + lane;
       const int row = qq / 4, part = swz_slot<4>(row, qq % 4) - row * 4;
-      q.b_off[i] = (uint32_t)(q.nb * BNW + row) * (uint32_t)(I / 2) + part * 16;
+      q.b_off[i] = (uint32_t)((q.nb * BNW + row) / 16) * (uint32_t)(8 * I) + 16 * (16 * part + row % 16);
     }
     const int sc_row = lw * WAVE + lane;
     q.as_on = HAS_AS && lw * WAVE < q.rows_used;
@@ -887,14 +889,14 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_kernel(FusedArgs p
   auto issue = [&](const Src& q, int s, int buf) {
     const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * F::BUF);
     const uint8_t* ab = q.a + s * KA;
-    const uint8_t* bb = q.b + s * 64;
+    const uint8_t* bb = q.b + s * 1024;
 #pragma unroll
     for (int i = 0; i < F::A_IPL; ++i)
       if (i < q.n_ai) dma16(ab, q.a_off[i], L + (i * NLOAD + lw) * 1024);
     if (!q.b_on) return;
 #pragma unroll
     for (int i = 0; i < F::B_IPL; ++i)
-      dma16(bb, q.b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
+      dma16nt(bb, q.b_off[i], L + F::A_BYTES + (i * NLOAD + lw) * 1024);
     if (q.as_on) dma4(q.as + s * 4, q.as_off, L + F::A_BYTES + F::B_BYTES + lw * 256);
     dma4(q.bs + s * 4, q.bs_off, L + F::A_BYTES + F::B_BYTES + BM * 4 + lw * 256);
   };
@@ -1133,7 +1135,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedAr
     const int j = i * NLOAD + lw;
     const int qq = j * WAVE + lane;
     const int row = qq / 4, part = swz_slot<4>(row, qq % 4) - row * 4;
-    b_off[i] = (uint32_t)row * (uint32_t)(I / 2) + part * 16;
+    b_off[i] = (uint32_t)(row / 16) * (uint32_t)(8 * I) + 16 * (16 * part + row % 16);
   }
   const int sc_row = lw * WAVE + lane;
   const uint32_t bs_off = (uint32_t)sc_row * (uint32_t)(I / 32);
@@ -1176,9 +1178,9 @@ __global__ __launch_bounds__(GTHREADS, 1) void grouped_stage2_res_kernel(FusedAr
     auto issue_b = [&](int t) {
       const int c = t / S, s = t - c * S;
       const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + R::A_REGION + (t % P2) * R::B_BUF);
-      const uint8_t* bb = qb + (size_t)(cb0 + c) * BNW * (I / 2) + s * 64;
+      const uint8_t* bb = qb + (size_t)(cb0 + c) * BNW * (I / 2) + s * 1024;
 #pragma unroll
-      for (int i = 0; i < F::B_IPL; ++i) dma16(bb, b_off[i], L + (i * NLOAD + lw) * 1024);
+      for (int i = 0; i < F::B_IPL; ++i) dma16nt(bb, b_off[i], L + (i * NLOAD + lw) * 1024);
       dma4(qbs + (size_t)(cb0 + c) * BNW * (I / 32) + s * 4, bs_off, L + F::B_BYTES + lw * 256);
     };
 
@@ -1511,7 +1513,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
     const int e = s_hot[hh];
     const uint32_t L = __builtin_amdgcn_readfirstlane(lds0 + buf * F::BUF);
     const uint8_t* ab = p.inter + s * KA;
-    const uint8_t* bb = p.w2 + (size_t)e * D * (I / 2) + s * 64;
+    const uint8_t* bb = p.w2 + (size_t)e * D * (I / 2) + s * 1024;
 #pragma unroll
     for (int i = 0; i < F::A_IPL; ++i) {
       const int j = i * NLOAD + lw;
@@ -1525,7 +1527,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void hot_stage2_kernel(FusedArgs p, in
       const int j = i * NLOAD + lw;
       const int q = j * WAVE + lane;
       const int row = q / 4, part = swz_slot<4>(row, q % 4) - row * 4;
-      dma16(bb, (uint32_t)(nb * BNW + row) * (uint32_t)(I / 2) + part * 16, L + F::A_BYTES + j * 1024);
+      dma16(bb, (uint32_t)((nb * BNW + row) / 16) * (uint32_t)(8 * I) + 16 * (16 * part + row % 16),
+            L + F::A_BYTES + j * 1024);
     }
     const int sc = lw * WAVE + lane;
     if (lw * WAVE < BM) {

@@ -113,8 +113,10 @@ constexpr int TILED_MIN_TOKENS_S1 = 2048;   // Stage1 from this batch size
 constexpr int TILED_MIN_TOKENS_S2 = 2048;   // Stage2 from this batch size
 static_assert(TILED_MIN_TOKENS_S1 <= TILED_MIN_TOKENS_S2, "Stage2 reads Stage1's tile groups");
 
-// Stage1 weights [E, 2I, D/2] row-major -> the packed layout of moe_pack.hip (same size).
+// Stage1 weights [E, 2I, D/2] and Stage2 weights [E, D, I/2] row-major -> the packed layout of
+// moe_pack.hip (same size).
 hipError_t launch_pack_w1(const uint8_t* w1, uint8_t* out, int E, int D, int I, hipStream_t s);
+hipError_t launch_pack_w2(const uint8_t* w2, uint8_t* out, int E, int D, int I, hipStream_t s);
 
 // Single-launch path (moe_single.hip): Stage1, Stage2 and the combine in one grid whose
 // workgroups signal each other through the layout's sync words.

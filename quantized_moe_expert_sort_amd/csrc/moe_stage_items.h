@@ -426,7 +426,9 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
   for (int j = 0; j < NF; ++j) {
     const int n = nb * NO + wave * NF * 16 + 16 * j + r16;
     const size_t wr = (size_t)e * D + n;
-    brow[j] = p.w2 + wr * (I / 2);
+    // packed w2 (moe_pack.hip): the 16 rows of fragment j at K step s are the 1 KB block at
+    // (fragment's first row) * I/2 + 1024 s, lane l's 16 bytes at 16 l
+    brow[j] = p.w2 + (wr - r16) * (I / 2) + 16 * lane;
     bsrow[j] = p.w2s + wr * (I / 32);
   }
   v4f acc[MF][NF];
@@ -482,7 +484,7 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
       for (int i = 0; i < PF; ++i)
         if (FULL || i < S)
 #pragma unroll
-          for (int j = 0; j < NF; ++j) bq[i][j] = ld16(brow[j] + i * 64 + 16 * g);
+          for (int j = 0; j < NF; ++j) bq[i][j] = ldw16(brow[j] + i * 1024);
       __builtin_amdgcn_sched_barrier(0);
       // the copies were issued before this wave's weight loads; the barrier makes every wave's
       // copies visible
@@ -516,7 +518,7 @@ __device__ __forceinline__ bool stage2_item(const FusedArgs& p, int tile, int nb
     for (int j = 0; j < NF; ++j) {
 #pragma unroll
       for (int i = 0; i < PF; ++i)
-        if (s0 + i < S) bq[i][j] = ld16(brow[j] + (s0 + i) * 64 + 16 * g);
+        if (s0 + i < S) bq[i][j] = ldw16(brow[j] + (s0 + i) * 1024);
       bsq[j].load(bsrow[j], s0, S, g, true);
     }
   };

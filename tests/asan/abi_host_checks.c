@@ -75,7 +75,7 @@ static void sort_checks(void) {
 
 /* moe_fused with the default valid arguments, each case changing one of them */
 typedef struct {
-  int32_t a_dtype, w1_layout, T, K, E, D, I, stages;
+  int32_t a_dtype, w_layout, T, K, E, D, I, stages;
   const void *x, *xs;
   uint16_t *out;
   moe_layout_t *L;
@@ -86,7 +86,7 @@ typedef struct {
 static fused_args fused_default(void) {
   fused_args a;
   memset(&a, 0, sizeof(a));
-  a.a_dtype = MOE_DT_BF16; a.w1_layout = MOE_W1_PACKED;
+  a.a_dtype = MOE_DT_BF16; a.w_layout = MOE_W_PACKED;
   a.T = 4; a.K = 2; a.E = 8; a.D = 256; a.I = 128; a.stages = MOE_STAGE_ALL;
   a.x = P; a.xs = NULL; a.out = (uint16_t *)P;
   a.L = layout(moe_cap_tiles(a.T, a.K, a.E, 16), 16, 1, 1);
@@ -96,12 +96,12 @@ static fused_args fused_default(void) {
 }
 
 static int fused(const fused_args *a) {
-  return moe_fused(a->x, (const uint8_t *)a->xs, a->a_dtype, P, a->w1_layout, P, P, P, P, a->L, a->T, a->K,
+  return moe_fused(a->x, (const uint8_t *)a->xs, a->a_dtype, P, a->w_layout, P, P, P, P, a->L, a->T, a->K,
                    a->E, a->D, a->I, a->act, a->out, P, a->ws_bytes, a->stages, NULL);
 }
 
 static int fused_noalloc(const fused_args *a) {
-  return moe_fused_noalloc(a->x, (const uint8_t *)a->xs, a->a_dtype, P, a->w1_layout, P, P, P, P, a->L, a->T,
+  return moe_fused_noalloc(a->x, (const uint8_t *)a->xs, a->a_dtype, P, a->w_layout, P, P, P, P, a->L, a->T,
                            a->K, a->E, a->D, a->I, a->act, a->out, a->stages, NULL);
 }
 
@@ -133,8 +133,9 @@ static void fused_checks(int noalloc) {
   CASE((free(a.L), a.L = NULL), MOE_ERR_INVALID_ARG);
   CASE(a.stages = 0, MOE_ERR_INVALID_ARG);
   CASE(a.stages = 4, MOE_ERR_INVALID_ARG);
-  CASE(a.w1_layout = MOE_W1_ROW_MAJOR, MOE_ERR_UNSUPPORTED);
-  CASE(a.w1_layout = 2, MOE_ERR_INVALID_ARG);
+  CASE(a.w_layout = MOE_W_ROW_MAJOR, MOE_ERR_UNSUPPORTED);
+  CASE(a.w_layout = MOE_W1_PACKED, MOE_ERR_UNSUPPORTED);
+  CASE(a.w_layout = 3, MOE_ERR_INVALID_ARG);
   CASE(a.T = 0, MOE_OK);
   if (!noalloc) CASE(a.ws_bytes = 10, MOE_ERR_WORKSPACE);
   if (noalloc) {
@@ -155,18 +156,19 @@ static void quant_checks(void) {
   EXPECT(moe_quant_act(P, 0, 64, MOE_DT_FP4_E2M1, P, P, NULL), MOE_OK);
 }
 
-static void pack_checks(void) {
+typedef moe_status_t (*pack_fn)(const uint8_t *, int32_t, int32_t, int32_t, uint8_t *, void *);
+
+static void pack_checks(pack_fn pack, size_t n /* bytes of the weights at E = 2, D = 256, I = 128 */) {
   uint8_t *w = (uint8_t *)P;
   uint8_t *other = (uint8_t *)0x4000000;
-  const size_t n = (size_t)2 * 2 * 128 * 128;   /* w1 bytes at E = 2, D = 256, I = 128 */
-  EXPECT(moe_pack_w1(w, 2, 256, 128, w, NULL), MOE_ERR_INVALID_ARG);
-  EXPECT(moe_pack_w1(w, 2, 256, 128, w + n - 16, NULL), MOE_ERR_INVALID_ARG);
-  EXPECT(moe_pack_w1(w + 16, 2, 256, 128, w, NULL), MOE_ERR_INVALID_ARG);
-  EXPECT(moe_pack_w1(NULL, 2, 256, 128, other, NULL), MOE_ERR_INVALID_ARG);
-  EXPECT(moe_pack_w1(w, 2, 256, 128, NULL, NULL), MOE_ERR_INVALID_ARG);
-  EXPECT(moe_pack_w1(w, 0, 256, 128, other, NULL), MOE_ERR_INVALID_ARG);
-  EXPECT(moe_pack_w1(w, 2, 192, 128, other, NULL), MOE_ERR_UNSUPPORTED);
-  EXPECT(moe_pack_w1(w, 2, 256, 64, other, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(pack(w, 2, 256, 128, w, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(pack(w, 2, 256, 128, w + n - 16, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(pack(w + 16, 2, 256, 128, w, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(pack(NULL, 2, 256, 128, other, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(pack(w, 2, 256, 128, NULL, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(pack(w, 0, 256, 128, other, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(pack(w, 2, 192, 128, other, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(pack(w, 2, 256, 64, other, NULL), MOE_ERR_UNSUPPORTED);
 }
 
 int main(void) {
@@ -174,7 +176,8 @@ int main(void) {
   fused_checks(0);
   fused_checks(1);
   quant_checks();
-  pack_checks();
+  pack_checks(moe_pack_w1, (size_t)2 * 256 * 128);   /* [E, 2I, D/2] */
+  pack_checks(moe_pack_w2, (size_t)2 * 256 * 64);    /* [E, D, I/2] */
   EXPECT(moe_last_hip_error(), 0);   /* nothing above reached the HIP runtime */
   if (failures) {
     fprintf(stderr, "%d check(s) failed\n", failures);

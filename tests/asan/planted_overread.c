@@ -21,7 +21,7 @@ int main(void) {
   L->row_of = (int32_t *)P;
   L->cap_tiles = 100;
   L->block_m = 16;
-  const int st = moe_fused(P, NULL, MOE_DT_BF16, P, MOE_W1_PACKED, P, P, P, P, L, 4, 2, 8, 256, 128, a,
+  const int st = moe_fused(P, NULL, MOE_DT_BF16, P, MOE_W_PACKED, P, P, P, P, L, 4, 2, 8, 256, 128, a,
                            (uint16_t *)P, P, (size_t)1 << 30, MOE_STAGE_ALL, NULL);
   printf("status %d\n", st);
   free(a);

@@ -114,10 +114,10 @@ def test_sort_validation():
 
 
 def _fused(a_dtype=0, xs=None, act=0, beta=4.0, lb=25.0, T=4, K=2, E=8, D=256, I=128, layout=None,
-           ws_bytes=1 << 30, out=P, x=P, stages=3, w1_layout=1):
+           ws_bytes=1 << 30, out=P, x=P, stages=3, w_layout=2):
     lay = _layout(cap=qm.cap_tiles(T, K, E, 16)) if layout is None else layout
     ap = qm.ActParams(act, beta, lb)
-    return qm.lib().moe_fused(x, xs, a_dtype, P, w1_layout, P, P, P, P, ctypes.byref(lay), T, K, E, D, I,
+    return qm.lib().moe_fused(x, xs, a_dtype, P, w_layout, P, P, P, P, ctypes.byref(lay), T, K, E, D, I,
                               ctypes.byref(ap), out, P, ws_bytes, stages, None)
 
 
@@ -139,9 +139,10 @@ def test_fused_validation():
     assert _fused(layout=_layout(cap=100, row_of=False)) == INVALID   # the combine needs row_of
     assert _fused(stages=0) == INVALID
     assert _fused(stages=4) == INVALID
-    assert _fused(w1_layout=0) == UNSUPPORTED           # row-major w1: pack it with moe_pack_w1 first
-    assert _fused(w1_layout=2) == INVALID
-    assert _fused(w1_layout=0, T=0) == UNSUPPORTED      # the tag is checked before anything else
+    assert _fused(w_layout=0) == UNSUPPORTED            # row-major weights: pack both first
+    assert _fused(w_layout=1) == UNSUPPORTED            # w1 packed, w2 row-major: pack w2 too
+    assert _fused(w_layout=3) == INVALID
+    assert _fused(w_layout=0, T=0) == UNSUPPORTED       # the tag is checked before anything else
     assert _fused(T=0) == OK                            # empty batch: nothing to do
 
 
@@ -149,13 +150,14 @@ def test_fused_validation():
 def test_fused_noalloc_validation():
     f = qm.lib().moe_fused_noalloc
 
-    def call(a_dtype=0, xs=None, T=4, K=2, E=8, D=256, I=128, cap=None, bm=16, w1_layout=1, act=0):
+    def call(a_dtype=0, xs=None, T=4, K=2, E=8, D=256, I=128, cap=None, bm=16, w_layout=2, act=0):
         lay = _layout(cap=qm.cap_tiles(T, K, E, bm) if cap is None else cap, bm=bm)
         ap = qm.ActParams(act, 4.0, 25.0)
-        return f(P, xs, a_dtype, P, w1_layout, P, P, P, P, ctypes.byref(lay), T, K, E, D, I, ctypes.byref(ap), P,
+        return f(P, xs, a_dtype, P, w_layout, P, P, P, P, ctypes.byref(lay), T, K, E, D, I, ctypes.byref(ap), P,
                  3, None)
     assert call(a_dtype=7) == INVALID
-    assert call(w1_layout=0) == UNSUPPORTED
+    assert call(w_layout=0) == UNSUPPORTED
+    assert call(w_layout=1) == UNSUPPORTED
     assert call(act=9) == UNSUPPORTED
     assert call(D=200) == UNSUPPORTED
     assert call(cap=1) == CAPACITY
@@ -184,11 +186,12 @@ def test_quant_validation():
 
 
 @no_gpu
-def test_pack_validation():
-    f = qm.lib().moe_pack_w1
+@pytest.mark.parametrize("which", ["moe_pack_w1", "moe_pack_w2"])
+def test_pack_validation(which):
+    f = getattr(qm.lib(), which)
     P2 = ctypes.c_void_p(8192)
     assert f(P, 2, 256, 128, P, None) == INVALID        # in place
-    n = 2 * 2 * 128 * 128                               # bytes of w1 at E=2, D=256, I=128
+    n = 2 * 2 * 128 * 128 if which == "moe_pack_w1" else 2 * 256 * 64   # bytes at E=2, D=256, I=128
     assert f(P, 2, 256, 128, ctypes.c_void_p(P.value + n - 16), None) == INVALID   # overlap at the end
     assert f(ctypes.c_void_p(P.value + 16), 2, 256, 128, P, None) == INVALID       # overlap at the start
     assert f(None, 2, 256, 128, P2, None) == INVALID

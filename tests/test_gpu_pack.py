@@ -1,5 +1,5 @@
-"""moe_pack_w1 on the GPU: the packed Stage1 weight layout is a pure reordering of the bytes,
-checked byte for byte against the layout the ABI header states, written out with numpy."""
+"""moe_pack_w1 and moe_pack_w2 on the GPU: the packed weight layouts are pure reorderings of the
+bytes, checked byte for byte against the layout the ABI header states, written out with numpy."""
 import numpy as np
 import pytest
 import torch
@@ -25,3 +25,26 @@ def test_pack_w1_matches_stated_layout(E, D, I):
     got = qm.moe_pack_w1(torch.from_numpy(w1).cuda())
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), packed_reference(w1))
+
+
+@pytest.mark.parametrize("E,D,I", [(1, 128, 128), (3, 512, 256), (5, 384, 384), (2, 3584, 384)])
+def test_pack_w2_matches_stated_layout(E, D, I):
+    rng = np.random.default_rng(E * 7000 + D + I)
+    w2 = rng.integers(0, 256, size=(E, D, I // 2), dtype=np.uint8)
+    got = qm.moe_pack_w2(torch.from_numpy(w2).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), packed_reference(w2))
+
+
+def test_pack_w2_into_the_bytes_right_after_it():
+    # w2 holds E*D*I/2 bytes (half of w1's E*2I*D/2): a packed buffer that starts right after it
+    # does not overlap and must be accepted
+    E, D, I = 2, 256, 128
+    rng = np.random.default_rng(5)
+    w2 = rng.integers(0, 256, size=(E, D, I // 2), dtype=np.uint8)
+    buf = torch.empty(2 * w2.size, dtype=torch.uint8, device="cuda")
+    src, dst = buf[:w2.size], buf[w2.size:]
+    src.copy_(torch.from_numpy(w2.reshape(-1)).cuda())
+    qm.moe_pack_w2(src.view(E, D, I // 2), out=dst.view(E, D, I // 2))
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.view(E, D, I // 2).cpu().numpy(), packed_reference(w2))
