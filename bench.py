@@ -270,8 +270,8 @@ def spin_cycles_per_ms():
 
 
 def is_hbm_bound(wl, r):
-    """The workload's bound from its own measured work (SURVEY's rule): HBM when streaming the
-    touched weights at 8 TB/s takes longer than the flops at the dtype's MFMA peak."""
+    """The workload's bound from its own measured work: HBM when streaming the touched weights
+    at 8 TB/s takes longer than the flops at the dtype's MFMA peak."""
     return r["weight_bytes"] / (HBM_PEAK_GBPS * 1e9) >= r["flops"] / (MFMA_PEAK_TFLOPS[wl.a_dtype] * 1e12)
 
 
