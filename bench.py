@@ -507,6 +507,33 @@ def counter_summarize(fetch_dir, write_dir, mfma_dir):
     return "\n".join(lines)
 
 
+def gpu_info():
+    """The device's power cap, model and clocks from rocm-smi, run as a child process right after
+    the headline's timed passes (the clocks are those of a loaded GPU); None where rocm-smi is
+    missing or prints something else.  The power cap matters: the pages saw 15-19% swings from
+    it."""
+    card = None
+    for exe in ("rocm-smi", "/opt/rocm/bin/rocm-smi"):
+        try:
+            out = subprocess.run([exe, "--showmaxpower", "--showclocks", "--showproductname", "--json"],
+                                 capture_output=True, text=True, timeout=30).stdout
+            card = next(iter(json.loads(out).values()))
+            break
+        except Exception:
+            continue
+    if not isinstance(card, dict):
+        return None
+    keys = {"power_cap_w": "Max Graphics Package Power (W)", "sclk": "sclk clock speed:",
+            "mclk": "mclk clock speed:", "gfx": "GFX Version", "model": "Card Model"}
+    info = {k: card.get(v) for k, v in keys.items() if v in card}
+    try:
+        import torch
+        info["name"] = torch.cuda.get_device_properties(0).name
+    except Exception:
+        pass
+    return info or None
+
+
 # ---------------------------------------------------------------------------------- oracle
 
 def cpu_info():
@@ -646,6 +673,7 @@ def main():
     wb = Workbench(wl, args.routings, dev_w)
     log(f"timing {args.steps} steps after {args.warmup} warmup")
     r = wb.run(args.steps, args.warmup, graph_calls=200)
+    gpu = gpu_info()
     s = summarize(wl, r)
     log(f"{wl.name}: {s}")
     cpu = None
@@ -703,6 +731,7 @@ def main():
         "touched_experts": s["touched_experts"],
         "roofline": s["roofline"], "cpu_baseline": cpu,
         "host_cpu": {"model": model, "cores_available": avail, "blas_threads": blas},
+        "gpu": gpu,
         "tiers": tiers,
     }
     print(json.dumps(line), flush=True)
