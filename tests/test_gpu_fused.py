@@ -113,6 +113,11 @@ SMALL = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, act, zipf)
     # the same batch sizes with model_dim % 512 != 0 take the per-tile stages
     (2500, 40, 6, 256, 128, 0, 40, 32, "fp4", "silu", 0.0),
     (3000, 64, 8, 768, 384, 16, 24, 32, "fp8", "situv2", 0.0),
+    # the smallest shape (one K step each way, a Stage2 column block wider than model_dim) at
+    # the decode kernel's limit and one row past it, and top-1 routing
+    (3, 40, 11, 128, 128, 0, 40, 16, "fp8", "situv2", 0.0),      # 33 routed rows: per-tile Stage2
+    (1, 8, 8, 128, 128, 0, 8, 32, "fp4", "silu", 0.0),           # one token, 32-row tiles
+    (32, 16, 1, 128, 256, 0, 16, 16, "bf16", "situv2", 0.0),     # top-1: exactly 32 routed rows
 ]
 
 
