@@ -3,7 +3,8 @@
 * Valid inputs: every call returns MOE_OK and the sorted layout and the output are
   bit-identical to the normal library's (the checks only read), on the decode kernel, the
   per-tile stages at block_m 16 and 32, an expert-parallel shard, the large-batch grouped stages
-  with hot experts, and the single-launch path.
+  (with a few hot experts, and with every expert hot: the token-major Stage2), and the
+  single-launch path.
 * Corrupted layouts, each chosen so that the corrupted access stays inside allocated memory even
   if its check were missing: a row_of entry one row past the layout (the combine's read of that
   row would land in the workspace part after the per-row outputs), a sorted row id past
@@ -72,6 +73,7 @@ VALID = [  # (T, E_router, K, D, I, eb, E_local, bm, a_dtype, zipf, single_launc
     (4096, 512, 8, 512, 256, 0, 512, 32, "fp8", 0.7, False),    # grouped stages, hot experts
     (2048, 16, 4, 512, 256, 0, 16, 32, "bf16", 1.1, False),     # grouped bf16 Stage1
     (6, 32, 8, 256, 128, 0, 32, 16, "fp8", 0.0, True),          # single-launch path
+    (2048, 24, 16, 512, 256, 0, 24, 32, "fp4", 0.3, False),     # token-major Stage2 of hot experts
 ]
 
 
