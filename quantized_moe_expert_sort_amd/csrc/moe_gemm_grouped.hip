@@ -330,7 +330,8 @@ struct GFmt {
   static constexpr int KA = ADT == DT_FP8 ? 128 : ADT == DT_FP4 ? 64 : 256;   // A bytes per row per K step
   static constexpr int ACPR = KA / 16;                    // 16-byte chunks per A row
   static constexpr int P = ADT == DT_FP4 ? 4 : 3;         // LDS buffers = K steps in flight + 1
-  static constexpr int AD = ADT == DT_FP8 ? 2 : ADT == DT_FP4 ? 3 : 1;   // A fragments read ahead of the MFMAs
+  // A fragments read ahead of the MFMAs (fp8: 1 measured 1.2% faster than 2 in the Stage1)
+  static constexpr int AD = ADT == DT_FP4 ? 3 : 1;
   static constexpr int A_BYTES = BM * KA;
   static constexpr int B_BYTES = BNW * 64;
   static constexpr int BUF = A_BYTES + B_BYTES + (BM + BNW) * 4;   // Stage2: + per-step scale dwords
